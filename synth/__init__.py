@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for the Prism hot path (shared by the tests, the benchmark and
+the smoke check).  This module holds no arithmetic of the method itself: it only draws
+token fields, audio norms and output gradients, and rounds them to the compute dtype.
+
+Workloads.  The pages train and evaluate on private 720p/1080p/2K video latents and on a
+300-video 2K benchmark; none is available, so these token grids stand in for them (a 2K
+clip gives "hundreds of thousands to over one million tokens" per the reading guide's
+"Problem and motivation").  Per config i (1..5) the generator uses
+``np.random.SeedSequence(1000 + i).spawn(8)``, one child per array in the order
+f, phi, noise_Q, noise_K, noise_V, audio centres, audio noise, dO (PCG64 each).
+
+* Field: per zone m integer cycles f[m, axis] in {0..3}; per (m, head, channel, axis) a
+  phase phi in [0, 2pi).  F(x) = sum_axis cos(2 pi f x_axis / 8 + phi), x_axis in 0..7 the
+  local zone coordinate.  Q = A_qk F + N(0,1), K = A_qk F + N(0,1), V = A_v F + N(0,1)
+  (shared F, independent noise), layout [N, heads, d], token n = (t*H + h)*W + w.
+* Audio norm per token: |N(0, 0.1^2)| + sum of Gaussian blobs of peak 1 and sigma 4
+  tokens, centres uniform on [0,T) x [0,H) x [0,W).
+* bf16 configs are rounded once, round-to-nearest-even, on the host; the arrays returned
+  here hold exactly the rounded values (as float32), so both sides see the same numbers.
+* Attention scale sm_scale = gamma / sqrt(d).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    H: int
+    W: int
+    heads: int
+    d: int
+    dtype: str            # "f32" or "bf16"
+    blobs: int
+    k_abs: int            # > 0: absolute Top-k count
+    k_frac: float         # used when k_abs == 0: k = ceil(k_frac * N_b)
+    p: float              # Top-p cumulative-probability threshold
+    backward: bool
+    seed: int
+    amp_qk: float = 1.0
+    amp_v: float = 1.0
+    gamma: float = 16.0
+    groups: int = 1
+    tau128: float = 0.5
+    tau256: float = 0.25
+    eps: float = 1e-6
+    blob_sigma: float = 4.0
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def Z(self) -> int:
+        return self.N // 512
+
+    @property
+    def nbmax(self) -> int:
+        return 8 * self.Z
+
+    @property
+    def sm_scale(self) -> float:
+        return self.gamma / math.sqrt(self.d)
+
+    def replace(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+CONFIGS = {
+    # tiny forward: 8x16x16 grid (4 zones), 2 heads, d 64, fp32, k = 2 blocks
+    "tiny": Config("tiny", 8, 16, 16, 2, 64, "f32", blobs=1, k_abs=2, k_frac=0.0, p=0.9,
+                   backward=False, seed=1001),
+    # 720p-shaped forward
+    "720p": Config("720p", 24, 48, 80, 8, 128, "bf16", blobs=3, k_abs=0, k_frac=0.05, p=0.9,
+                   backward=False, seed=1002),
+    # 1080p-shaped forward + backward
+    "1080p": Config("1080p", 24, 72, 120, 8, 128, "bf16", blobs=4, k_abs=0, k_frac=0.05, p=0.9,
+                    backward=True, seed=1003),
+    # 2K-shaped forward + backward (headline)
+    "2k": Config("2k", 32, 96, 160, 4, 128, "bf16", blobs=6, k_abs=0, k_frac=0.05, p=0.9,
+                 backward=True, seed=1004),
+    # 2K dispersed-attention stress: field amplitude 0.1 on V (near-isotropic zones), logits
+    # scaled by 0.3, k = 2 %, p = 0.95
+    "2k_stress": Config("2k_stress", 32, 96, 160, 4, 128, "bf16", blobs=6, k_abs=0, k_frac=0.02,
+                        p=0.95, backward=True, seed=1005, amp_v=0.1, gamma=16.0 * 0.3),
+}
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round-to-nearest-even) and widen back, exactly."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def make_inputs(cfg: Config, with_dout: bool | None = None) -> dict:
+    """Draw one layer's inputs.  Returns float32 arrays (bf16-exact for bf16 configs):
+    q, k, v [N, heads, d], a [N], dout [N, heads, d] or None, plus the scalar knobs."""
+    T, H, W, heads, d = cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d
+    if T % 8 or H % 8 or W % 8:
+        raise ValueError("grid must be a multiple of 8 on every axis")
+    ZT, ZH, ZW = T // 8, H // 8, W // 8
+    Z, N = ZT * ZH * ZW, T * H * W
+    ss = np.random.SeedSequence(cfg.seed).spawn(8)
+    rng = [np.random.default_rng(s) for s in ss]
+
+    f = rng[0].integers(0, 4, size=(Z, 3))                                  # cycles per zone, axis
+    phi = rng[1].uniform(0.0, 2.0 * np.pi, size=(Z, heads, d, 3))
+    i8 = np.arange(8, dtype=np.float64)
+    # per-axis profile tables [Z, heads, d, 8]
+    prof = [np.cos(2.0 * np.pi * f[:, ax, None, None, None] * i8 / 8.0 + phi[..., ax, None])
+            for ax in range(3)]
+    shape6 = (ZT, ZH, ZW, heads, d, 8)
+    pT, pH, pW = (p_.reshape(shape6).astype(np.float32) for p_ in prof)
+    # F[zt, lt, zh, lh, zw, lw, head, ch]
+    F = (pT.transpose(0, 5, 1, 2, 3, 4)[:, :, :, None, :, None, :, :]
+         + pH.transpose(0, 1, 5, 2, 3, 4)[:, None, :, :, :, None, :, :]
+         + pW.transpose(0, 1, 2, 5, 3, 4)[:, None, :, None, :, :, :, :])
+    F = np.ascontiguousarray(F, dtype=np.float32).reshape(N, heads, d)
+    del prof, pT, pH, pW
+
+    def noisy(amp, g):
+        x = g.standard_normal((N, heads, d), dtype=np.float32)
+        x += np.float32(amp) * F
+        return x
+
+    q = noisy(cfg.amp_qk, rng[2])
+    k = noisy(cfg.amp_qk, rng[3])
+    v = noisy(cfg.amp_v, rng[4])
+    del F
+
+    centres = rng[5].uniform(0.0, 1.0, size=(cfg.blobs, 3)) * np.array([T, H, W], np.float64)
+    a = np.abs(rng[6].normal(0.0, 0.1, size=N))
+    tt, hh, ww = np.meshgrid(np.arange(T, dtype=np.float64), np.arange(H, dtype=np.float64),
+                             np.arange(W, dtype=np.float64), indexing="ij")
+    for c in centres:
+        r2 = (tt - c[0]) ** 2 + (hh - c[1]) ** 2 + (ww - c[2]) ** 2
+        a += np.exp(-r2.reshape(-1) / (2.0 * cfg.blob_sigma ** 2))
+    a = a.astype(np.float32)
+
+    want_do = cfg.backward if with_dout is None else with_dout
+    dout = rng[7].standard_normal((N, heads, d), dtype=np.float32) if want_do else None
+
+    if cfg.dtype == "bf16":
+        q, k, v = _round_bf16(q), _round_bf16(k), _round_bf16(v)
+        if dout is not None:
+            dout = _round_bf16(dout)
+    elif cfg.dtype != "f32":
+        raise ValueError(f"unknown dtype {cfg.dtype}")
+
+    return dict(cfg=cfg, q=q, k=k, v=v, a=a, dout=dout, sm_scale=cfg.sm_scale, k_abs=cfg.k_abs,
+                k_frac=cfg.k_frac, p=cfg.p, tau128=cfg.tau128, tau256=cfg.tau256, eps=cfg.eps)
