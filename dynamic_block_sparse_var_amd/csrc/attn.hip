@@ -1,0 +1,307 @@
+// attn.hip -- block-sparse attention (RG M3: online-softmax attention solely across S_i):
+// launch logic, backward helpers, and the fp32 path.
+//
+// bf16 problems run the MFMA kernels of attn_mfma.hip.  fp32 problems run the kernels below:
+// one thread per query row (forward, dQ) or key row (dK/dV), fp32 FMA, expf/logf.  They are
+// the plain-precision path for fp32 inputs, not tuned.
+//
+// Backward helpers shared by both paths:
+//   k_fill_u32   zero fill (used instead of a memset so the call stays graph-capturable),
+//   k_mask_t     transposed selection bitmap: bit i of word [h][j][i/32] set when j in S_i,
+//                built with atomicOr (order-independent, so deterministic),
+//   k_delta      delta_r = dO_r . O_r in fp32.
+#include <math.h>
+
+#include "attn_common.h"
+
+namespace prism {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void st<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_ref_fwd(const T* __restrict__ q, const T* __restrict__ k,
+                                                const T* __restrict__ v, T* __restrict__ o, float* __restrict__ lse,
+                                                const int32_t* __restrict__ block_start,
+                                                const int32_t* __restrict__ sel_count,
+                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int64_t N,
+                                                float sm_scale) {
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * 64 + threadIdx.x;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  const int i = block_of_row(bs, nbmax, blockIdx.x * 64);
+  const int cnt = sel_count[(int64_t)h * nbmax + i];
+  const int32_t* list = sel_idx + ((int64_t)h * nbmax + i) * nbmax;
+  const int64_t hb = (int64_t)h * N;
+  float qr[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qr[e] = ld(q, (hb + row) * D + e);
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int s = 0; s < cnt; ++s) {
+    const int j = list[s];
+    for (int c = bs[j]; c < bs[j + 1]; ++c) {
+      float z = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) z = fmaf(qr[e], ld(k, (hb + c) * D + e), z);
+      z *= sm_scale;
+      const float mn = fmaxf(m, z);
+      const float alpha = expf(m - mn), pz = expf(z - mn);
+      l = l * alpha + pz;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(pz, ld(v, (hb + c) * D + e), acc[e] * alpha);
+      m = mn;
+    }
+  }
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) st(o, (hb + row) * D + e, acc[e] * inv);
+  lse[hb + row] = (l > 0.f) ? m + logf(l) : -INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_ref_dq(const T* __restrict__ q, const T* __restrict__ k,
+                                               const T* __restrict__ v, const T* __restrict__ dout,
+                                               const float* __restrict__ lse, const float* __restrict__ delta,
+                                               T* __restrict__ dq, const int32_t* __restrict__ block_start,
+                                               const int32_t* __restrict__ sel_count,
+                                               const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int64_t N,
+                                               float sm_scale) {
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * 64 + threadIdx.x;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  const int i = block_of_row(bs, nbmax, blockIdx.x * 64);
+  const int cnt = sel_count[(int64_t)h * nbmax + i];
+  const int32_t* list = sel_idx + ((int64_t)h * nbmax + i) * nbmax;
+  const int64_t hb = (int64_t)h * N;
+  float qr[D], dor[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qr[e] = ld(q, (hb + row) * D + e);
+    dor[e] = ld(dout, (hb + row) * D + e);
+    acc[e] = 0.f;
+  }
+  const float L = lse[hb + row], dl = delta[hb + row];
+  for (int s = 0; s < cnt; ++s) {
+    const int j = list[s];
+    for (int c = bs[j]; c < bs[j + 1]; ++c) {
+      float z = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        z = fmaf(qr[e], ld(k, (hb + c) * D + e), z);
+        dp = fmaf(dor[e], ld(v, (hb + c) * D + e), dp);
+      }
+      const float pz = expf(z * sm_scale - L);
+      const float ds = pz * (dp - dl);
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, ld(k, (hb + c) * D + e), acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < D; ++e) st(dq, (hb + row) * D + e, acc[e] * sm_scale);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const T* __restrict__ k,
+                                                 const T* __restrict__ v, const T* __restrict__ dout,
+                                                 const float* __restrict__ lse, const float* __restrict__ delta,
+                                                 T* __restrict__ dk, T* __restrict__ dv,
+                                                 const int32_t* __restrict__ block_start,
+                                                 const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
+                                                 int64_t N, float sm_scale) {
+  const int h = blockIdx.y;
+  const int key = blockIdx.x * 64 + threadIdx.x;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  const int j = block_of_row(bs, nbmax, blockIdx.x * 64);
+  const uint32_t* mrow = mask_t + ((int64_t)h * nbmax + j) * nw;
+  const int64_t hb = (int64_t)h * N;
+  float kr[D], vr[D], adk[D], adv[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    kr[e] = ld(k, (hb + key) * D + e);
+    vr[e] = ld(v, (hb + key) * D + e);
+    adk[e] = adv[e] = 0.f;
+  }
+  for (int w = 0; w < nw; ++w) {
+    uint32_t bits = mrow[w];
+    while (bits) {
+      const int i = (w << 5) + __ffs(bits) - 1;
+      bits &= bits - 1;
+      for (int r = bs[i]; r < bs[i + 1]; ++r) {
+        float z = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) {
+          z = fmaf(ld(q, (hb + r) * D + e), kr[e], z);
+          dp = fmaf(ld(dout, (hb + r) * D + e), vr[e], dp);
+        }
+        const float pz = expf(z * sm_scale - lse[hb + r]);
+        const float ds = pz * (dp - delta[hb + r]);
+#pragma unroll
+        for (int e = 0; e < D; ++e) {
+          adv[e] = fmaf(pz, ld(dout, (hb + r) * D + e), adv[e]);
+          adk[e] = fmaf(ds, ld(q, (hb + r) * D + e), adk[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    st(dk, (hb + key) * D + e, adk[e] * sm_scale);
+    st(dv, (hb + key) * D + e, adv[e]);
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t val) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = val;
+}
+
+__global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, const int32_t* __restrict__ block_start,
+                                                const int32_t* __restrict__ sel_count,
+                                                const int32_t* __restrict__ sel_idx, int nbmax, int nw, int hpg,
+                                                int64_t N) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  if (bs[i] >= N) return;
+  const int64_t row = (int64_t)h * nbmax + i;
+  const int cnt = sel_count[row];
+  const int32_t* list = sel_idx + row * nbmax;
+  for (int s = threadIdx.x; s < cnt; s += 256) {
+    const int j = list[s];
+    atomicOr(&mask_t[((int64_t)h * nbmax + j) * nw + (i >> 5)], 1u << (i & 31));
+  }
+}
+
+// delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T* __restrict__ dout,
+                                               float* __restrict__ delta, int64_t rows) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int LPR = D / EPC;  // lanes per row (8..32)
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gt / LPR;
+  const int part = (int)(gt % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * EPC);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + part * EPC);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(bf16_lo(wa[i]), bf16_lo(wb[i]), fmaf(bf16_hi(wa[i]), bf16_hi(wb[i]), acc));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(wa[i]), __uint_as_float(wb[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+template <typename T, int D>
+prism_status run_ref_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
+                         const void* q, const void* k, const void* v, void* o, float* lse, hipStream_t st) {
+  dim3 grid((unsigned)(g.N / 64), g.heads);
+  hipLaunchKernelGGL((k_ref_fwd<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, bs,
+                     cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
+  return check_launch("k_ref_fwd");
+}
+
+template <typename T, int D>
+prism_status run_ref_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
+                         const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* delta, const uint32_t* mask_t, int nw, void* dq, void* dk, void* dv,
+                         hipStream_t st) {
+  dim3 grid((unsigned)(g.N / 64), g.heads);
+  hipLaunchKernelGGL((k_ref_dq<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
+                     (const T*)dout, lse, delta, (T*)dq, bs, cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
+  prism_status s = check_launch("k_ref_dq");
+  if (s != PRISM_OK) return s;
+  hipLaunchKernelGGL((k_ref_dkdv<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
+                     (const T*)dout, lse, delta, (T*)dk, (T*)dv, bs, mask_t, g.nbmax, nw, g.hpg, g.N, sm_scale);
+  return check_launch("k_ref_dkdv");
+}
+
+}  // namespace
+
+BwdWorkspace bwd_workspace_layout(const Geom& g) {
+  BwdWorkspace w;
+  w.nw = (g.nbmax + 31) / 32;
+  w.delta_off = 0;
+  const size_t delta_bytes = (size_t)g.heads * g.N * sizeof(float);
+  w.mask_off = (delta_bytes + 255) & ~(size_t)255;
+  const size_t mask_words = (size_t)g.heads * g.nbmax * w.nw;
+  w.mask_words = mask_words;
+  w.total = w.mask_off + ((mask_words * sizeof(uint32_t) + 255) & ~(size_t)255);
+  return w;
+}
+
+size_t bsa_bwd_workspace_bytes(const Geom& g) { return bwd_workspace_layout(g).total; }
+
+prism_status launch_bsa_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
+                            const void* q, const void* k, const void* v, void* o, float* lse, hipStream_t st) {
+  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
+  if (g.d == 64) return run_ref_fwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
+  return run_ref_fwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
+}
+
+prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
+                            const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+  const BwdWorkspace w = bwd_workspace_layout(g);
+  float* delta = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.delta_off);
+  uint32_t* mask_t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + w.mask_off);
+  // transposed selection
+  const int fill_blocks = (int)((w.mask_words + 255) / 256 < 4096 ? (w.mask_words + 255) / 256 : 4096);
+  hipLaunchKernelGGL(k_fill_u32, dim3(fill_blocks > 0 ? fill_blocks : 1), dim3(256), 0, st, mask_t,
+                     (int64_t)w.mask_words, 0u);
+  prism_status s = check_launch("k_fill_u32");
+  if (s != PRISM_OK) return s;
+  hipLaunchKernelGGL(k_mask_t, dim3(g.nbmax, g.heads), dim3(256), 0, st, mask_t, bs, cnt, idx, g.nbmax, w.nw, g.hpg,
+                     g.N);
+  s = check_launch("k_mask_t");
+  if (s != PRISM_OK) return s;
+  // delta
+  const int64_t rows = (int64_t)g.heads * g.N;
+  const int lpr = g.d * g.esize / 16;
+  const int64_t dblocks = (rows * lpr + 255) / 256;
+  if (g.bf16) {
+    if (g.d == 64)
+      hipLaunchKernelGGL((k_delta<uint16_t, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
+                         (const uint16_t*)dout, delta, rows);
+    else
+      hipLaunchKernelGGL((k_delta<uint16_t, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
+                         (const uint16_t*)dout, delta, rows);
+  } else {
+    if (g.d == 64)
+      hipLaunchKernelGGL((k_delta<float, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
+                         (const float*)dout, delta, rows);
+    else
+      hipLaunchKernelGGL((k_delta<float, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
+                         (const float*)dout, delta, rows);
+  }
+  s = check_launch("k_delta");
+  if (s != PRISM_OK) return s;
+  if (g.bf16) return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
+  if (g.d == 64)
+    return run_ref_bwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
+  return run_ref_bwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
+}
+
+}  // namespace prism

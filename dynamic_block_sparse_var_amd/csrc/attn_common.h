@@ -1,0 +1,24 @@
+// attn_common.h -- declarations shared by the attention sources (not part of the ABI).
+#pragma once
+
+#include "prism_internal.h"
+
+namespace prism {
+
+// Backward workspace: delta [heads, N] fp32, then the transposed selection bitmap
+// [heads, NBMAX, nw] uint32 (nw = ceil(NBMAX / 32)), each 256-byte aligned.
+struct BwdWorkspace {
+  size_t delta_off, mask_off, mask_words, total;
+  int nw;
+};
+BwdWorkspace bwd_workspace_layout(const Geom& g);
+
+prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
+                             float sm_scale, const void* q, const void* k, const void* v, void* o, float* lse,
+                             hipStream_t st);
+prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
+                             float sm_scale, const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* delta, const uint32_t* mask_t, int nw, void* dq,
+                             void* dk, void* dv, hipStream_t st);
+
+}  // namespace prism

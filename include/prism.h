@@ -1,0 +1,175 @@
+/* prism.h -- C ABI of the MI355X (gfx950) Prism hot path: content-adaptive dynamic
+ * block-sparse video self-attention, forward and backward, for one layer and head group.
+ *
+ * Sources.  "RG" is the reading-guide page of "Prism: Dynamic Sparse Attention for Native
+ * 2K Joint Video-Audio Generation Model Training" (arXiv 2610.05416).  RG M1, M2, M3 are its
+ * Method parts 1 ("Variation Indicator Formulation"), 2 ("Block Volume and Shape
+ * Quantization") and 3 ("Hybrid Top-k / Top-p Attention"); RG KI is its "Key ideas" list.
+ * "README" is the Prism project page (table "Core training parameters").
+ *
+ * Conventions shared by every call
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
+ *   nothing and keeps no state other than a per-thread error message.  Host arrays are
+ *   named as such.  `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * - Every call validates its arguments on the host first and returns an error code without
+ *   launching anything if they are bad.  On success it enqueues work on `stream` and returns;
+ *   results are valid once the stream reaches that point.  No exception crosses the ABI.
+ * - Tensors are contiguous; tensor pointers must be 16-byte aligned.
+ * - Token grid T x H x W, each a positive multiple of 8 (macro-zones of 8x8x8 tokens, RG KI),
+ *   N = T*H*W tokens, Z = N/512 zones, NBMAX = 8*Z (the most blocks a group can have).
+ *   Token order n = (t*H + h)*W + w; token-order tensors are [N, heads, head_dim].
+ *   Zone order m = (zt*(H/8) + zh)*(W/8) + zw.
+ * - Block order: zones in zone order, the blocks of a zone in raster order over the zone's
+ *   block grid, the tokens of a block in raster order.  Block-order tensors are
+ *   [heads, N, head_dim]; block j of group g covers rows [block_start[g][j], block_start[g][j+1]).
+ * - heads are split into `groups` head groups of heads/groups consecutive heads; each group
+ *   has its own zone statistics, shapes and block layout; selection and attention are per head.
+ * - dtype PRISM_BF16: bf16 tensors, fp32 accumulation.  PRISM_F32: fp32 tensors throughout.
+ * - Limits: head_dim in {64, 128}; Z <= 1024 (N <= 524,288 tokens; the selection sorts a
+ *   query block's scores in one workgroup's LDS).
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PRISM_ABI_VERSION 1
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_E_NULL = 1,      /* a required pointer is NULL */
+  PRISM_E_SHAPE = 2,     /* grid / heads / head_dim / groups not supported */
+  PRISM_E_RANGE = 3,     /* a scalar argument is out of range */
+  PRISM_E_DTYPE = 4,     /* unknown dtype */
+  PRISM_E_ALIGN = 5,     /* a tensor pointer is not 16-byte aligned */
+  PRISM_E_WORKSPACE = 6, /* workspace too small */
+  PRISM_E_HIP = 7        /* a HIP runtime call failed (detail in prism_last_error) */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+typedef struct {
+  int32_t T, H, W;   /* token grid, each a positive multiple of 8 */
+  int32_t heads;     /* attention heads in this call */
+  int32_t head_dim;  /* 64 or 128 */
+  int32_t groups;    /* head groups (heads % groups == 0) */
+  int32_t dtype;     /* prism_dtype of Q, K, V, O and their gradients */
+} prism_problem;
+
+/* ---- information ------------------------------------------------------------------- */
+
+int32_t prism_abi_version(void);
+const char* prism_status_string(prism_status s);
+/* Detail of the last failing call on this thread ("" if none).  Owned by the library. */
+const char* prism_last_error(void);
+/* The 16-shape candidate set (RG KI; volumes {64,128,256}, RG M2), in the library's index
+ * order: volume ascending, then (b_T, b_H, b_W) lexicographic, edges in {2,4,8}.
+ * Writes 48 int32 into the HOST array edges ([16][3]); returns 16. */
+int32_t prism_shape_table(int32_t* edges);
+
+/* ---- a1: zone statistics (RG M1) ---------------------------------------------------- *
+ * For each head group g and zone m, over the group's D = (heads/groups)*head_dim channels:
+ *   sigma^2_{v,d}(m) = (1/D) sum_c (1/8) sum_i (Vbar^{(d)}_{m,i,c} - mu_{m,c})^2, where
+ *   Vbar^{(d)}_{m,i,c} is the mean of channel c over the 64 tokens of slice i along axis d and
+ *   mu_{m,c} the zone mean (the variation-ratio equation of RG M1);
+ *   r_{v,d} = sigma^2_{v,d} / sum_d' sigma^2_{v,d'} (1/3 each if the sum is 0);
+ *   rho(m) = sum_d sigma^2_{v,d} / sigma^2_tok, sigma^2_tok = (1/D) sum_c (1/512) sum_x
+ *     (V_{x,c} - mu_c)^2 (0 if sigma^2_tok = 0) -- the reading of RG M2's "normalized
+ *     spatiotemporal information density";
+ *   audio (reading of RG M1's abar and vhat): A(m) = zone mean of a, abar = A / max_m' A(m'),
+ *   vhat_d = the same directional variance applied to the field a, normalised to sum 1
+ *   (1/3 each if flat); abar = vhat = 0 when a is NULL (no cached norms yet);
+ *   g_d(m) = r_{v,d} + abar * vhat_d + eps (composite-indicator equation of RG M1).
+ * v:          [N, heads, head_dim] dtype, token order (the layer's values).
+ * a:          [N] fp32 audio-to-video cross-attention output norms from the preceding layer,
+ *             or NULL.
+ * eps:        > 0.
+ * g:          out [groups, Z, 3] fp32 (axes T, H, W).
+ * rho:        out [groups, Z] fp32.
+ * zone_audio: out [Z, 4] fp32 = (abar, vhat_T, vhat_H, vhat_W); required when a != NULL,
+ *             ignored (may be NULL) when a == NULL. */
+prism_status prism_zone_stats(const prism_problem* pb, const void* v, const float* a, float eps,
+                              float* g, float* rho, float* zone_audio, void* stream);
+
+/* ---- a2: block volume and shape (RG M2) --------------------------------------------- *
+ * B(m) = 64 if rho >= tau128, 128 if tau256 <= rho < tau128, else 256 (RG M2 thresholds;
+ * denser zones get smaller blocks).  l*_d = -1/2 log2 g_d + 1/3 (log2 B + 1/2 sum log2 g)
+ * (RG M2 log2-space optimum); the shape is the candidate of volume B nearest to l* in
+ * Euclidean log2 distance (lowest index on exact ties).  Decisions are taken in fp32.
+ * tau128, tau256: 0 <= tau256 <= tau128.
+ * shape_idx:      out [groups, Z] uint8, index into prism_shape_table.
+ * zone_block_off: out [groups, Z+1] int32, exclusive scan of 512/B(m); [g][Z] = N_b(g).
+ * block_start:    out [groups, NBMAX+1] int32, first block-order row of block j; entries
+ *                 j >= N_b(g) hold N. */
+prism_status prism_assign_shapes(const prism_problem* pb, const float* g, const float* rho,
+                                 float tau128, float tau256, uint8_t* shape_idx,
+                                 int32_t* zone_block_off, int32_t* block_start, void* stream);
+
+/* ---- a3: token order <-> block order ------------------------------------------------ *
+ * Moves rows between token order [N, heads, head_dim] and block order [heads, N, head_dim]
+ * using each group's shape map (the block order described above; the pages ask that each
+ * block's tokens be kept together, RG M3 / abstract).  inverse = 0: token -> block order;
+ * inverse = 1: block -> token order.  count (1..4) tensors per call: src and dst are HOST
+ * arrays of `count` device pointers, dtype per pb.  src and dst must not overlap. */
+prism_status prism_permute(const prism_problem* pb, const uint8_t* shape_idx, int32_t inverse,
+                           int32_t count, const void* const* src, void* const* dst, void* stream);
+
+/* ---- a4: pooled block representatives (RG M3) --------------------------------------- *
+ * xbar[h][j][:] = mean of rows [block_start[j], block_start[j+1]) of x_perm[h] (fp32
+ * accumulation), zero for j >= N_b.  count (1..4) tensors: x_perm is a HOST array of device
+ * pointers to [heads, N, head_dim] dtype tensors, xbar a HOST array of device pointers to
+ * [heads, NBMAX, head_dim] fp32 outputs. */
+prism_status prism_pool_blocks(const prism_problem* pb, const int32_t* block_start, int32_t count,
+                               const void* const* x_perm, float* const* xbar, void* stream);
+
+/* ---- a5: hybrid Top-k / Top-p block selection (RG M3 attended-set equation) ---------- *
+ * Per head h and query block i < N_b: s_ij = sm_scale * qbar_i . kbar_j (fp32), P_i = softmax
+ * over the N_b key blocks, order by P descending (block index ascending on ties),
+ * n_p = smallest n with cumulative P >= p (0 if p == 0; N_b if never reached),
+ * k = clamp(k_abs > 0 ? k_abs : ceil(k_frac * N_b), 1, N_b) evaluated in double
+ * (README: bsa_sparsity s keeps a fraction 1 - s), S_i = the first max(k, n_p) blocks of
+ * that order (the union of the two prefixes), written in ascending block order.
+ * qbar, kbar: [heads, NBMAX, head_dim] fp32 from prism_pool_blocks.
+ * sel_count:  out [heads, NBMAX] int32 (0 for i >= N_b).
+ * sel_idx:    out [heads, NBMAX, NBMAX] int32, row (h, i) holds S_i in its first
+ *             sel_count entries.  The whole array is also used as fp32 score scratch during
+ *             the call; entries past sel_count are unspecified afterwards.
+ * k_abs >= 0, 0 <= k_frac <= 1, 0 <= p <= 1, sm_scale finite and > 0. */
+prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_start,
+                                 const float* qbar, const float* kbar, float sm_scale,
+                                 int32_t k_abs, double k_frac, double p, int32_t* sel_count,
+                                 int32_t* sel_idx, void* stream);
+
+/* ---- a6: block-sparse attention forward (RG M3: online-softmax attention solely across S_i)
+ * For head h and each row r of query block i (block order): exact softmax over every key
+ * row of the blocks in S_i of sm_scale * q_r . k_c, O_r = sum p v_c, LSE_r natural log
+ * (-inf and O = 0 for an empty list).  No causal mask, dropout or bias.
+ * q, k, v, o: [heads, N, head_dim] dtype, block order.  lse: out [heads, N] fp32. */
+prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
+                           const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
+                           const void* q, const void* k, const void* v, void* o, float* lse,
+                           void* stream);
+
+/* ---- a7: block-sparse attention backward -------------------------------------------- *
+ * Gradient of prism_bsa_fwd with the selection held constant: delta_r = dO_r . O_r,
+ * P = exp(sm_scale q.k - LSE), dV = P^T dO, dS = P (dO v^T - delta), dQ = sm_scale dS K,
+ * dK = sm_scale dS^T Q.  o and lse are prism_bsa_fwd's outputs for the same inputs.
+ * dq, dk, dv: out [heads, N, head_dim] dtype, block order (fully overwritten).
+ * workspace: device scratch of at least prism_bsa_bwd_workspace_bytes(pb) bytes, 256-byte
+ * aligned; its contents on entry do not matter. */
+size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb);
+prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
+                           const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
+                           const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PRISM_H */

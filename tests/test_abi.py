@@ -1,0 +1,99 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function include/prism.h
+declares, reports the candidate table the oracle enumerates independently, and rejects bad
+arguments with the documented status before any HIP call."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import dynamic_block_sparse_var_amd as P
+import oracle
+
+
+@pytest.fixture(scope="module")
+def L():
+    return P.lib()
+
+
+def test_exports_every_header_function(L):
+    names = P.header_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert P.prism_abi_version() == 1
+
+
+def test_shape_table_matches_oracle_enumeration():
+    edges, _ = oracle.candidates()
+    assert P.prism_shape_table() == [tuple(e) for e in edges.tolist()]
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.prism_status_string(s)
+
+
+def _pb(**kw):
+    base = dict(T=8, H=16, W=16, heads=2, head_dim=64, groups=1, dtype=P.BF16)
+    base.update(kw)
+    return P.Problem(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), 2), (dict(T=12), 2), (dict(W=4), 2), (dict(heads=0), 2), (dict(head_dim=96), 2),
+    (dict(groups=3), 2), (dict(dtype=7), 4), (dict(T=8, H=8 * 64, W=8 * 32), 2),
+])
+def test_bad_problem_rejected(L, kw, status):
+    pb = _pb(**kw)
+    rc = L.prism_zone_stats(ctypes.byref(pb), FAKE, None, 1e-6, FAKE, FAKE, None, None)
+    assert rc == status, L.prism_last_error()
+    assert L.prism_last_error()
+
+
+def test_null_and_alignment_rejected(L):
+    pb = _pb()
+    assert L.prism_zone_stats(None, FAKE, None, 1e-6, FAKE, FAKE, None, None) == 1
+    assert L.prism_zone_stats(ctypes.byref(pb), None, None, 1e-6, FAKE, FAKE, None, None) == 1
+    assert L.prism_zone_stats(ctypes.byref(pb), MISALIGNED, None, 1e-6, FAKE, FAKE, None, None) == 5
+    # audio given but no zone_audio output
+    assert L.prism_zone_stats(ctypes.byref(pb), FAKE, FAKE, 1e-6, FAKE, FAKE, None, None) == 1
+    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+
+
+def test_scalar_ranges_rejected(L):
+    pb = _pb()
+    assert L.prism_zone_stats(ctypes.byref(pb), FAKE, None, 0.0, FAKE, FAKE, None, None) == 3
+    assert L.prism_assign_shapes(ctypes.byref(pb), FAKE, FAKE, 0.2, 0.3, FAKE, FAKE, FAKE, None) == 3
+    assert L.prism_assign_shapes(ctypes.byref(pb), FAKE, FAKE, 0.5, -0.1, FAKE, FAKE, FAKE, None) == 3
+    sel = L.prism_select_blocks
+    assert sel(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.1, -1, 0.0, 0.5, FAKE, FAKE, None) == 3
+    assert sel(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.1, 0, 1.5, 0.5, FAKE, FAKE, None) == 3
+    assert sel(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.1, 0, 0.05, 1.01, FAKE, FAKE, None) == 3
+    assert sel(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.0, 0, 0.05, 0.5, FAKE, FAKE, None) == 3
+    assert sel(ctypes.byref(pb), FAKE, FAKE, FAKE, float("nan"), 2, 0.0, 0.5, FAKE, FAKE, None) == 3
+    arr = (ctypes.c_void_p * 5)(*([0x10000] * 5))
+    assert L.prism_permute(ctypes.byref(pb), FAKE, 2, 1, arr, arr, None) == 3
+    assert L.prism_permute(ctypes.byref(pb), FAKE, 0, 5, arr, arr, None) == 3
+    assert L.prism_pool_blocks(ctypes.byref(pb), FAKE, 0, arr, arr, None) == 3
+
+
+def test_backward_workspace(L):
+    pb = _pb()
+    need = P.prism_bsa_bwd_workspace_bytes(pb)
+    N, nb = 8 * 16 * 16, 8 * 4
+    assert need >= 2 * N * 4 + 2 * nb * ((nb + 31) // 32) * 4
+    args = [ctypes.byref(pb)] + [FAKE] * 3 + [0.125] + [FAKE] * 9
+    assert L.prism_bsa_bwd(*args, FAKE, need - 1, None) == 6
+    assert L.prism_bsa_bwd(*args, MISALIGNED, need, None) == 5
+    assert P.prism_bsa_bwd_workspace_bytes(_pb(T=3)) == 0
+
+
+def test_selection_capacity_limit(L):
+    # 1024 zones is the largest grid; 1025+ must be refused up front
+    pb = _pb(T=8, H=8 * 32, W=8 * 33)
+    assert L.prism_zone_stats(ctypes.byref(pb), FAKE, None, 1e-6, FAKE, FAKE, None, None) == 2
+    assert np.isfinite(0.0)
