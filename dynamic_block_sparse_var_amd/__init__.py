@@ -85,9 +85,9 @@ def lib():
         "prism_permute": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp, _vp]),
         "prism_pool_blocks": (_i32, [_PB, _vp, _i32, _vp, _vp, _vp]),
         "prism_select_blocks": (_i32, [_PB, _vp, _vp, _vp, _f32, _i32, _f64, _f64, _vp, _vp, _vp]),
-        "prism_bsa_fwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "prism_bsa_fwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "prism_bsa_bwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
-        "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
     }
     for name, (res, args) in sig.items():
@@ -164,21 +164,21 @@ def prism_select_blocks(pb, block_start, qbar, kbar, sm_scale, k_abs, k_frac, p,
            "prism_select_blocks")
 
 
-def prism_bsa_fwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, lse, stream=None):
+def prism_bsa_fwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, stream=None):
     _check(lib().prism_bsa_fwd(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale, _p(q), _p(k),
-                               _p(v), _p(o), _p(lse), _stream(stream)), "prism_bsa_fwd")
+                               _p(v), _p(o), _p(o_lo), _p(lse), _stream(stream)), "prism_bsa_fwd")
 
 
 def prism_bsa_bwd_workspace_bytes(pb) -> int:
     return int(lib().prism_bsa_bwd_workspace_bytes(ctypes.byref(pb)))
 
 
-def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, dout, lse, dq, dk, dv, workspace,
                   stream=None):
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().prism_bsa_bwd(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale, _p(q), _p(k),
-                               _p(v), _p(o), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv), _p(workspace), nbytes,
-                               _stream(stream)), "prism_bsa_bwd")
+                               _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv), _p(workspace),
+                               nbytes, _stream(stream)), "prism_bsa_bwd")
 
 
 # ---- one layer -------------------------------------------------------------------------
@@ -209,14 +209,16 @@ class PrismLayer:
         self.sel_count = torch.empty(H_, NB, dtype=torch.int32, **e)
         self.sel_idx = torch.empty(H_, NB, NB, dtype=torch.int32, **e)
         self.op = torch.empty_like(self.qp)
+        # rounding residual of O (bf16 only), kept for an accurate backward
+        self.op_lo = torch.empty_like(self.qp) if (backward and pb.dtype == BF16) else None
         self.lse = torch.empty(H_, N, dtype=torch.float32, **e)
         self.o = torch.empty(N, H_, d, dtype=dt, **e)
         if backward:
             self.dop = torch.empty_like(self.qp)
-            self.dqp = torch.empty_like(self.qp)
-            self.dkp = torch.empty_like(self.qp)
-            self.dvp = torch.empty_like(self.qp)
-            self.dq = torch.empty(N, H_, d, dtype=dt, **e)
+            self.dqp = torch.empty(H_, N, d, dtype=torch.float32, **e)
+            self.dkp = torch.empty_like(self.dqp)
+            self.dvp = torch.empty_like(self.dqp)
+            self.dq = torch.empty(N, H_, d, dtype=torch.float32, **e)
             self.dk = torch.empty_like(self.dq)
             self.dv = torch.empty_like(self.dq)
             nbytes = prism_bsa_bwd_workspace_bytes(pb)
@@ -240,7 +242,7 @@ class PrismLayer:
     def attend(self, sm_scale, stream=None):
         pb = self.pb
         prism_bsa_fwd(pb, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp, self.kp, self.vp,
-                      self.op, self.lse, stream)
+                      self.op, self.op_lo, self.lse, stream)
         prism_permute(pb, self.shape_idx, 1, [self.op], [self.o], stream)
         return self.o
 
@@ -254,8 +256,10 @@ class PrismLayer:
         pb = self.pb
         prism_permute(pb, self.shape_idx, 0, [dout], [self.dop], stream)
         prism_bsa_bwd(pb, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp, self.kp, self.vp,
-                      self.op, self.dop, self.lse, self.dqp, self.dkp, self.dvp, self.workspace, stream)
-        prism_permute(pb, self.shape_idx, 1, [self.dqp, self.dkp, self.dvp], [self.dq, self.dk, self.dv], stream)
+                      self.op, self.op_lo, self.dop, self.lse, self.dqp, self.dkp, self.dvp, self.workspace, stream)
+        # gradients are fp32: move them with an fp32 view of the same geometry
+        pb32 = Problem(pb.T, pb.H, pb.W, pb.heads, pb.head_dim, pb.groups, F32)
+        prism_permute(pb32, self.shape_idx, 1, [self.dqp, self.dkp, self.dvp], [self.dq, self.dk, self.dv], stream)
         return self.dq, self.dk, self.dv
 
 

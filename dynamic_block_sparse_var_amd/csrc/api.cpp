@@ -198,7 +198,7 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
 
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start, const int32_t* sel_count,
                            const int32_t* sel_idx, float sm_scale, const void* q, const void* k, const void* v,
-                           void* o, float* lse, void* stream) {
+                           void* o, void* o_lo, float* lse, void* stream) {
   g_err[0] = 0;
   PRISM_TRY(validate_problem(pb));
   PRISM_TRY(need_aligned(block_start, "block_start"));
@@ -208,10 +208,13 @@ prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start, 
   PRISM_TRY(need_aligned(k, "k"));
   PRISM_TRY(need_aligned(v, "v"));
   PRISM_TRY(need_aligned(o, "o"));
+  if (o_lo) PRISM_TRY(need_aligned(o_lo, "o_lo"));
   PRISM_TRY(need_aligned(lse, "lse"));
-  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
   Geom gm = make_geom(pb);
-  return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, lse, (hipStream_t)stream);
+  return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, lse,
+                        (hipStream_t)stream);
 }
 
 size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb) {
@@ -222,8 +225,8 @@ size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb) {
 
 prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, const int32_t* sel_count,
                            const int32_t* sel_idx, float sm_scale, const void* q, const void* k, const void* v,
-                           const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const void* o, const void* o_lo, const void* dout, const float* lse, float* dq, float* dk,
+                           float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   PRISM_TRY(validate_problem(pb));
   PRISM_TRY(need_aligned(block_start, "block_start"));
@@ -233,6 +236,7 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, 
   PRISM_TRY(need_aligned(k, "k"));
   PRISM_TRY(need_aligned(v, "v"));
   PRISM_TRY(need_aligned(o, "o"));
+  if (o_lo) PRISM_TRY(need_aligned(o_lo, "o_lo"));
   PRISM_TRY(need_aligned(dout, "dout"));
   PRISM_TRY(need_aligned(lse, "lse"));
   PRISM_TRY(need_aligned(dq, "dq"));
@@ -240,13 +244,14 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, 
   PRISM_TRY(need_aligned(dv, "dv"));
   PRISM_TRY(need_ptr(workspace, "workspace"));
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PRISM_E_ALIGN, "workspace not 256-byte aligned");
-  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
   Geom gm = make_geom(pb);
   size_t need = bsa_bwd_workspace_bytes(gm);
   if (workspace_bytes < need)
     return fail(PRISM_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  return launch_bsa_bwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                        (hipStream_t)stream);
+  return launch_bsa_bwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, dout,
+                        lse, dq, dk, dv, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

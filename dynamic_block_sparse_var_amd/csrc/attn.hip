@@ -78,7 +78,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void k_ref_dq(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const T* __restrict__ dout,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
-                                               T* __restrict__ dq, const int32_t* __restrict__ block_start,
+                                               float* __restrict__ dq, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int64_t N,
                                                float sm_scale) {
@@ -113,14 +113,14 @@ __global__ __launch_bounds__(64) void k_ref_dq(const T* __restrict__ q, const T*
     }
   }
 #pragma unroll
-  for (int e = 0; e < D; ++e) st(dq, (hb + row) * D + e, acc[e] * sm_scale);
+  for (int e = 0; e < D; ++e) dq[(hb + row) * D + e] = acc[e] * sm_scale;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                  const T* __restrict__ v, const T* __restrict__ dout,
                                                  const float* __restrict__ lse, const float* __restrict__ delta,
-                                                 T* __restrict__ dk, T* __restrict__ dv,
+                                                 float* __restrict__ dk, float* __restrict__ dv,
                                                  const int32_t* __restrict__ block_start,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
                                                  int64_t N, float sm_scale) {
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const 
   }
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    st(dk, (hb + key) * D + e, adk[e] * sm_scale);
-    st(dv, (hb + key) * D + e, adv[e]);
+    dk[(hb + key) * D + e] = adk[e] * sm_scale;
+    dv[(hb + key) * D + e] = adv[e];
   }
 }
 
@@ -187,10 +187,12 @@ __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, c
   }
 }
 
-// delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step
+// delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step.  O = o + o_lo when the
+// forward stored its rounding residual.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T* __restrict__ dout,
-                                               float* __restrict__ delta, int64_t rows) {
+__global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T* __restrict__ olo,
+                                               const T* __restrict__ dout, float* __restrict__ delta,
+                                               int64_t rows) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int LPR = D / EPC;  // lanes per row (8..32)
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -202,8 +204,16 @@ __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T*
     const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + part * EPC);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
     if constexpr (sizeof(T) == 2) {
+      uint32_t wl[4] = {0u, 0u, 0u, 0u};
+      if (olo) {
+        const uint4 c = *reinterpret_cast<const uint4*>(olo + row * D + part * EPC);
+        wl[0] = c.x; wl[1] = c.y; wl[2] = c.z; wl[3] = c.w;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(bf16_lo(wa[i]), bf16_lo(wb[i]), fmaf(bf16_hi(wa[i]), bf16_hi(wb[i]), acc));
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_lo(wa[i]) + bf16_lo(wl[i]), bf16_lo(wb[i]), acc);
+        acc = fmaf(bf16_hi(wa[i]) + bf16_hi(wl[i]), bf16_hi(wb[i]), acc);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(wa[i]), __uint_as_float(wb[i]), acc);
@@ -226,15 +236,15 @@ prism_status run_ref_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, c
 template <typename T, int D>
 prism_status run_ref_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                          const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                         const float* delta, const uint32_t* mask_t, int nw, void* dq, void* dk, void* dv,
+                         const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
                          hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   hipLaunchKernelGGL((k_ref_dq<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
-                     (const T*)dout, lse, delta, (T*)dq, bs, cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
+                     (const T*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
   prism_status s = check_launch("k_ref_dq");
   if (s != PRISM_OK) return s;
   hipLaunchKernelGGL((k_ref_dkdv<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
-                     (const T*)dout, lse, delta, (T*)dk, (T*)dv, bs, mask_t, g.nbmax, nw, g.hpg, g.N, sm_scale);
+                     (const T*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw, g.hpg, g.N, sm_scale);
   return check_launch("k_ref_dkdv");
 }
 
@@ -255,15 +265,17 @@ BwdWorkspace bwd_workspace_layout(const Geom& g) {
 size_t bsa_bwd_workspace_bytes(const Geom& g) { return bwd_workspace_layout(g).total; }
 
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
-                            const void* q, const void* k, const void* v, void* o, float* lse, hipStream_t st) {
-  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
+                            const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
+                            hipStream_t st) {
+  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, o_lo, lse, st);
   if (g.d == 64) return run_ref_fwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
   return run_ref_fwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
 }
 
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
-                            const void* q, const void* k, const void* v, const void* o, const void* dout,
-                            const float* lse, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+                            const void* q, const void* k, const void* v, const void* o, const void* o_lo,
+                            const void* dout, const float* lse, float* dq, float* dk, float* dv, void* ws,
+                            hipStream_t st) {
   const BwdWorkspace w = bwd_workspace_layout(g);
   float* delta = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.delta_off);
   uint32_t* mask_t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + w.mask_off);
@@ -284,17 +296,17 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   if (g.bf16) {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<uint16_t, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)dout, delta, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, delta, rows);
     else
       hipLaunchKernelGGL((k_delta<uint16_t, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)dout, delta, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, delta, rows);
   } else {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<float, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)dout, delta, rows);
+                         (const float*)nullptr, (const float*)dout, delta, rows);
     else
       hipLaunchKernelGGL((k_delta<float, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)dout, delta, rows);
+                         (const float*)nullptr, (const float*)dout, delta, rows);
   }
   s = check_launch("k_delta");
   if (s != PRISM_OK) return s;

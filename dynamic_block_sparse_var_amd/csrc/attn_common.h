@@ -14,11 +14,11 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(const Geom& g);
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
-                             float sm_scale, const void* q, const void* k, const void* v, void* o, float* lse,
-                             hipStream_t st);
+                             float sm_scale, const void* q, const void* k, const void* v, void* o, void* o_lo,
+                             float* lse, hipStream_t st);
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, const void* dout,
-                             const float* lse, const float* delta, const uint32_t* mask_t, int nw, void* dq,
-                             void* dk, void* dv, hipStream_t st);
+                             const float* lse, const float* delta, const uint32_t* mask_t, int nw, float* dq,
+                             float* dk, float* dv, hipStream_t st);
 
 }  // namespace prism

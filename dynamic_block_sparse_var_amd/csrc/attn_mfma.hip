@@ -55,6 +55,16 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int off) {
   return __builtin_convertvector(v, bf16x8);
 }
 
+// the same 8 elements as a bf16 head plus a bf16 residual: hi + lo carries ~16 significant bits
+__device__ __forceinline__ void pack8_split(const f32x16& x, int off, bf16x8& hi, bf16x8& lo) {
+  f32x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[off + i];
+  hi = __builtin_convertvector(v, bf16x8);
+  const f32x8 back = __builtin_convertvector(hi, f32x8);
+  lo = __builtin_convertvector(v - back, bf16x8);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -148,7 +158,8 @@ __device__ __forceinline__ void copy_out(uint16_t* __restrict__ dst, const uint1
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                                                float* __restrict__ LSE, const int32_t* __restrict__ block_start,
+                                                uint16_t* __restrict__ Olo, float* __restrict__ LSE,
+                                                const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                 float scale2) {
@@ -235,36 +246,49 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
     psum += __shfl_xor(psum, 32, 64);
     lrow = fmaf(lrow, alpha, psum);
     mrow = mnew;
-    bf16x8 pop[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) pop[t] = pack8(sacc[t >> 1], 8 * (t & 1));
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-    // O^T += V^T P^T
+    // O^T += V^T P^T, with P as bf16 head + residual so O keeps fp32-level accuracy (the
+    // backward's delta = dO . O cancels against dP and would expose bf16 rounding of P)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 p_hi, p_lo;
+      pack8_split(sacc[t >> 1], 8 * (t & 1), p_hi, p_lo);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        oacc[db] = mfma(as_bf16x8(lds16(sVt + (32 * db + l32) * C::TP + 16 * t + 8 * half)), pop[t], oacc[db]);
+      for (int db = 0; db < C::DB; ++db) {
+        const bf16x8 vt_op = as_bf16x8(lds16(sVt + (32 * db + l32) * C::TP + 16 * t + 8 * half));
+        oacc[db] = mfma(vt_op, p_hi, oacc[db]);
+        oacc[db] = mfma(vt_op, p_lo, oacc[db]);
+      }
+    }
     kt = nkt;
     sidx = nsidx;
     kend = nkend;
   }
   const float inv = (lrow > 0.f) ? 1.f / lrow : 0.f;
   if (half == 0) LSE[(int64_t)h * N + row0 + 32 * w + l32] = (lrow > 0.f) ? (mrow + log2f(lrow)) * kLn2 : -INFINITY;
-  __syncthreads();
   uint16_t* sO = sK;
+  // pass 0 writes O rounded to bf16, pass 1 (if requested) its rounding residual
+  for (int pass = 0; pass < (Olo ? 2 : 1); ++pass) {
+    __syncthreads();
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-      pk[1] = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-      *reinterpret_cast<u32x2*>(sO + (32 * w + l32) * C::KP + 32 * db + 8 * jj + 4 * half) = pk;
-    }
-  __syncthreads();
-  copy_out<D>(O + hoff + (int64_t)row0 * D, sO, tid);
+      for (int jj = 0; jj < 4; ++jj) {
+        float ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ov[e] = oacc[db][4 * jj + e] * inv;
+          if (pass) ov[e] -= bf16_to_f32(f32_to_bf16(ov[e]));
+        }
+        u32x2 pk;
+        pk[0] = pack_bf16x2(ov[0], ov[1]);
+        pk[1] = pack_bf16x2(ov[2], ov[3]);
+        *reinterpret_cast<u32x2*>(sO + (32 * w + l32) * C::KP + 32 * db + 8 * jj + 4 * half) = pk;
+      }
+    __syncthreads();
+    copy_out<D>((pass ? Olo : O) + hoff + (int64_t)row0 * D, sO, tid);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -274,7 +298,7 @@ template <int D>
 __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                const float* __restrict__ LSE, const float* __restrict__ delta,
-                                               uint16_t* __restrict__ dQ, const int32_t* __restrict__ block_start,
+                                               float* __restrict__ dQ, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                float scale2, float sm_scale) {
@@ -339,28 +363,32 @@ __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, c
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 dsop = pack8(sacc, 8 * tt);
+          bf16x8 ds_hi, ds_lo;
+          pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
           const int t = 2 * kb + tt;
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-            dqacc[db] = mfma(as_bf16x8(lds16(sKt + (32 * db + l32) * C::TP + 16 * t + 8 * half)), dsop, dqacc[db]);
+          for (int db = 0; db < C::DB; ++db) {
+            const bf16x8 kt_op = as_bf16x8(lds16(sKt + (32 * db + l32) * C::TP + 16 * t + 8 * half));
+            dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
+            dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
+          }
         }
       }
     }
   }
-  __syncthreads();
-  uint16_t* sO = sK;
+  // fp32 output: lane holds dQ[myrow][32db + 8jj + 4half + e]
+  float* dqr = dQ + hoff + (int64_t)myrow * D + 4 * half;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(dqacc[db][4 * jj + 0] * sm_scale, dqacc[db][4 * jj + 1] * sm_scale);
-      pk[1] = pack_bf16x2(dqacc[db][4 * jj + 2] * sm_scale, dqacc[db][4 * jj + 3] * sm_scale);
-      *reinterpret_cast<u32x2*>(sO + (32 * w + l32) * C::KP + 32 * db + 8 * jj + 4 * half) = pk;
+      float4 v4;
+      v4.x = dqacc[db][4 * jj + 0] * sm_scale;
+      v4.y = dqacc[db][4 * jj + 1] * sm_scale;
+      v4.z = dqacc[db][4 * jj + 2] * sm_scale;
+      v4.w = dqacc[db][4 * jj + 3] * sm_scale;
+      *reinterpret_cast<float4*>(dqr + 32 * db + 8 * jj) = v4;
     }
-  __syncthreads();
-  copy_out<D>(dQ + hoff + (int64_t)row0 * D, sO, tid);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -370,7 +398,7 @@ template <int D>
 __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                  const float* __restrict__ LSE, const float* __restrict__ delta,
-                                                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                                 float* __restrict__ dK, float* __restrict__ dV,
                                                  const int32_t* __restrict__ block_start,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
                                                  int N, float scale2, float sm_scale) {
@@ -461,75 +489,79 @@ __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q,
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const bf16x8 pa = pack8(sacc, 8 * t);
-            const bf16x8 da = pack8(dpacc, 8 * t);
+            bf16x8 pa_hi, pa_lo, da_hi, da_lo;
+            pack8_split(sacc, 8 * t, pa_hi, pa_lo);
+            pack8_split(dpacc, 8 * t, da_hi, da_lo);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
               const int off = (32 * db + l32) * C::TP + 32 * rb + 16 * t + 8 * half;
-              dvacc[db] = mfma(pa, as_bf16x8(lds16(sdOt + off)), dvacc[db]);
-              dkacc[db] = mfma(da, as_bf16x8(lds16(sQt + off)), dkacc[db]);
+              const bf16x8 dot_op = as_bf16x8(lds16(sdOt + off));
+              const bf16x8 qt_op = as_bf16x8(lds16(sQt + off));
+              dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
+              dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
+              dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
+              dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
             }
           }
         }
       }
     }
   }
-  // epilogue: accumulators hold [key = 8jj + 4half + e][d = 32db + l32]
-  __syncthreads();
-  uint16_t* sOk = sQ;
-  uint16_t* sOv = sdO;
+  // fp32 outputs: accumulators hold [key = 8jj + 4half + e][d = 32db + l32]; 32 lanes store
+  // 128 contiguous bytes of one key row per instruction
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * w + 8 * (r >> 2) + 4 * half + (r & 3);
-      sOk[key * C::KP + 32 * db + l32] = f32_to_bf16(dkacc[db][r] * sm_scale);
-      sOv[key * C::KP + 32 * db + l32] = f32_to_bf16(dvacc[db][r]);
+      const int key = key0 + 32 * w + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int64_t off = hoff + (int64_t)key * D + 32 * db + l32;
+      dK[off] = dkacc[db][r] * sm_scale;
+      dV[off] = dvacc[db][r];
     }
-  __syncthreads();
-  copy_out<D>(dK + hoff + (int64_t)key0 * D, sOk, tid);
-  copy_out<D>(dV + hoff + (int64_t)key0 * D, sOv, tid);
 }
 
 }  // namespace
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
-                             const void* q, const void* k, const void* v, void* o, float* lse, hipStream_t st) {
+                             const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
+                             hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   if (g.d == 64)
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)o, lse, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N, scale2);
+                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
+                       (int)g.N, scale2);
   else
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)o, lse, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N, scale2);
+                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
+                       (int)g.N, scale2);
   return check_launch("k_fwd");
 }
 
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                             const float* delta, const uint32_t* mask_t, int nw, void* dq, void* dk, void* dv,
+                             const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
                              hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   if (g.d == 64) {
     hipLaunchKernelGGL(k_dq<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, lse, delta, (uint16_t*)dq, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N,
+                       (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N,
                        scale2, sm_scale);
   } else {
     hipLaunchKernelGGL(k_dq<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, (uint16_t*)dq, bs, cnt, idx, g.nbmax,
+                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax,
                        g.hpg, (int)g.N, scale2, sm_scale);
   }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
   if (g.d == 64) {
     hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, (uint16_t*)dk, (uint16_t*)dv, bs,
+                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs,
                        mask_t, g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale);
   } else {
     hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, (uint16_t*)dk, (uint16_t*)dv, bs,
+                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs,
                        mask_t, g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale);
   }
   return check_launch("k_dkdv");

@@ -96,11 +96,12 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
                            double p, int32_t* sel_count, int32_t* sel_idx, hipStream_t st);
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
-                            const void* v, void* o, float* lse, hipStream_t st);
+                            const void* v, void* o, void* o_lo, float* lse, hipStream_t st);
 size_t bsa_bwd_workspace_bytes(const Geom& g);
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
-                            const void* v, const void* o, const void* dout, const float* lse,
-                            void* dq, void* dk, void* dv, void* ws, hipStream_t st);
+                            const void* v, const void* o, const void* o_lo, const void* dout,
+                            const float* lse, float* dq, float* dk, float* dv, void* ws,
+                            hipStream_t st);
 
 }  // namespace prism

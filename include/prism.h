@@ -149,25 +149,47 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
  * For head h and each row r of query block i (block order): exact softmax over every key
  * row of the blocks in S_i of sm_scale * q_r . k_c, O_r = sum p v_c, LSE_r natural log
  * (-inf and O = 0 for an empty list).  No causal mask, dropout or bias.
- * q, k, v, o: [heads, N, head_dim] dtype, block order.  lse: out [heads, N] fp32. */
+ * q, k, v, o: [heads, N, head_dim] dtype, block order.  lse: out [heads, N] fp32.
+ * o_lo: optional out [heads, N, head_dim] dtype (bf16 problems only; NULL to skip): the
+ *       rounding residual of O, o_lo = rnd(O_fp32 - o), so that o + o_lo carries about 16
+ *       significant bits.  prism_bsa_bwd uses it to form delta = dO . O without the bf16
+ *       rounding of o, which otherwise dominates the gradient error when the softmax is
+ *       peaked (dP - delta cancels). */
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
-                           const void* q, const void* k, const void* v, void* o, float* lse,
-                           void* stream);
+                           const void* q, const void* k, const void* v, void* o, void* o_lo,
+                           float* lse, void* stream);
 
 /* ---- a7: block-sparse attention backward -------------------------------------------- *
  * Gradient of prism_bsa_fwd with the selection held constant: delta_r = dO_r . O_r,
  * P = exp(sm_scale q.k - LSE), dV = P^T dO, dS = P (dO v^T - delta), dQ = sm_scale dS K,
- * dK = sm_scale dS^T Q.  o and lse are prism_bsa_fwd's outputs for the same inputs.
- * dq, dk, dv: out [heads, N, head_dim] dtype, block order (fully overwritten).
+ * dK = sm_scale dS^T Q.  o, o_lo and lse are prism_bsa_fwd's outputs for the same inputs
+ * (o_lo may be NULL; then delta uses o alone).
+ * dout: [heads, N, head_dim] dtype, block order.
+ * dq, dk, dv: out [heads, N, head_dim] fp32 for every dtype (gradients leave the fp32
+ *       accumulators unrounded), block order, fully overwritten.  For bf16 problems the
+ *       matrix-core products with P and dS split each factor into a bf16 head and a bf16
+ *       residual, so the gradients keep fp32-level accuracy.
  * workspace: device scratch of at least prism_bsa_bwd_workspace_bytes(pb) bytes, 256-byte
  * aligned; its contents on entry do not matter. */
 size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
                            const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           const void* o_lo, const void* dout, const float* lse, float* dq,
+                           float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ---- measurement hook --------------------------------------------------------------- *
+ * Records the HIP events start_event / stop_event (hipEvent_t passed as void*, created by
+ * the caller) immediately before and after every later launch of the library kernel named
+ * `kernel` (e.g. "k_fwd", "k_dq", "k_dkdv", "k_zone_stats", "k_permute", "k_pool",
+ * "k_scores", "k_select"), on that launch's stream, so a caller can time one kernel inside a
+ * multi-kernel call.  Up to 8 kernels can be traced at once; calling again with the same name
+ * replaces its events, and kernel == NULL clears every hook.  The hook is process-wide and
+ * not thread-safe; it is meant for benchmarks.  Returns PRISM_E_RANGE when all 8 slots are in
+ * use. */
+prism_status prism_trace_kernel(const char* kernel, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

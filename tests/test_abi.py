@@ -61,7 +61,9 @@ def test_null_and_alignment_rejected(L):
     assert L.prism_zone_stats(ctypes.byref(pb), MISALIGNED, None, 1e-6, FAKE, FAKE, None, None) == 5
     # audio given but no zone_audio output
     assert L.prism_zone_stats(ctypes.byref(pb), FAKE, FAKE, 1e-6, FAKE, FAKE, None, None) == 1
-    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, None, FAKE, None, FAKE, None) == 1
+    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE,
+                           None) == 5
 
 
 def test_scalar_ranges_rejected(L):
@@ -86,7 +88,7 @@ def test_backward_workspace(L):
     need = P.prism_bsa_bwd_workspace_bytes(pb)
     N, nb = 8 * 16 * 16, 8 * 4
     assert need >= 2 * N * 4 + 2 * nb * ((nb + 31) // 32) * 4
-    args = [ctypes.byref(pb)] + [FAKE] * 3 + [0.125] + [FAKE] * 9
+    args = [ctypes.byref(pb)] + [FAKE] * 3 + [0.125] + [FAKE] * 10
     assert L.prism_bsa_bwd(*args, FAKE, need - 1, None) == 6
     assert L.prism_bsa_bwd(*args, MISALIGNED, need, None) == 5
     assert P.prism_bsa_bwd_workspace_bytes(_pb(T=3)) == 0
