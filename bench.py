@@ -1,0 +1,313 @@
+#!/usr/bin/env python
+"""Benchmark of the Prism hot path on one MI355X.
+
+One step = one layer's whole path, forward and backward, on the 2K-shaped token grid
+32 x 96 x 160 (491,520 tokens, 960 zones), 4 heads, head_dim 128, bf16, k = 5 % of key
+blocks, p = 0.9 (seeded synthetic inputs of that shape; see synth/):
+
+  zone statistics -> volume/shape assignment -> permute Q,K,V -> pool Q,K -> select ->
+  sparse attention forward -> unpermute O -> permute dO -> sparse attention backward ->
+  unpermute dQ, dK, dV
+
+Printed: one JSON line.  ``value`` is ms per layer (whole step, lower is better).  Extra
+fields give per-stage times, attention TFLOP/s on executed (selected-block, algorithmic)
+FLOPs, the roofline of the dominant kernel (timed with HIP events recorded by the library
+around that kernel's launches), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config 2k] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
+MFMA_KERNELS = ("k_fwd", "k_dq", "k_dkdv")
+HBM_KERNELS = ("k_zone_stats", "k_pool")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "dynamic_block_sparse_var_amd", "csrc"))):
+        with open(os.path.join(ROOT, "dynamic_block_sparse_var_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def selection_stats(layer, pb):
+    """Executed query-key pairs from the GPU's own selection: sum over heads and query blocks
+    of |B_i| * sum_{j in S_i} |B_j|; also the mean key-token fraction and the B histogram."""
+    import torch
+
+    N, nbmax = pb.N, pb.nbmax
+    hpg = pb.heads // pb.groups
+    pairs = 0
+    frac = []
+    for h in range(pb.heads):
+        bs = layer.block_start[h // hpg].long()
+        sizes = (bs[1:] - bs[:-1]).clamp(min=0)
+        nb = int((bs[:-1] < N).sum())
+        ext = torch.cat([sizes, sizes.new_zeros(1)])
+        cnt = layer.sel_count[h, :nb].long()
+        keytok = torch.zeros(nb, dtype=torch.int64, device=bs.device)
+        for r0 in range(0, nb, 1024):
+            r1 = min(nb, r0 + 1024)
+            idx = layer.sel_idx[h, r0:r1, :].long()
+            col = torch.arange(nbmax, device=bs.device)[None, :]
+            idx = torch.where(col < cnt[r0:r1, None], idx, torch.full_like(idx, nbmax))
+            keytok[r0:r1] = ext[idx].sum(1)
+        pairs += int((sizes[:nb] * keytok).sum())
+        frac.append(float((keytok.double() / N).mean()))
+    vols = [64, 64, 64, 64, 64, 64, 64, 128, 128, 128, 128, 128, 128, 256, 256, 256]
+    sh = layer.shape_idx.cpu().numpy().reshape(-1)
+    hist = {64: 0, 128: 0, 256: 0}
+    for s in sh:
+        hist[vols[int(s)]] += 1
+    nblocks = int((layer.block_start[0, :-1] < N).sum())
+    return pairs, sum(frac) / len(frac), hist, nblocks
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    """The oracle as it stands, on the same inputs: the planning half (stats, shapes, block
+    layout, permute + pool of Q and K, full selection) timed in full, and the attention on a
+    sample of query blocks, extrapolated by executed query-key pairs."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    nth = oracle.default_threads()
+    cfg = inp["cfg"]
+    t0 = time.perf_counter()
+    orc = oracle.forward_path(inp, nthreads=nth)
+    t_plan = time.perf_counter() - t0
+    vp = oracle.permute(inp["v"], orc["pos"], cfg.heads)
+    dop = oracle.permute(inp["dout"], orc["pos"], cfg.heads)
+    bs, nb = orc["block_start"][0], int(orc["nblocks"][0])
+    sizes = np.diff(bs)[:nb].astype(np.int64)
+    rowpairs = np.zeros((cfg.heads, nb), np.int64)
+    for h in range(cfg.heads):
+        for i in range(nb):
+            rowpairs[h, i] = sizes[i] * sizes[orc["sel_idx"][h, i, :orc["sel_count"][h, i]]].sum()
+    total = int(rowpairs.sum())
+    rng = np.random.default_rng(0)
+    nq = max(1, nth // cfg.heads)
+    spent, t_fwd, t_bwd, pairs_s, rounds = 0.0, 0.0, 0.0, 0, 0
+    while spent < budget_s and rounds < 64:
+        mask = np.zeros((cfg.heads, cfg.nbmax), np.uint8)
+        for h in range(cfg.heads):
+            mask[h, rng.choice(nb, size=min(nq, nb), replace=False)] = 1
+        pairs_s += int(rowpairs[mask[:, :nb].astype(bool)].sum())
+        t0 = time.perf_counter()
+        oracle.attn_fwd(orc["qp"], orc["kp"], vp, orc["block_start"], orc["nblocks"], 1, orc["sel_count"],
+                        orc["sel_idx"], cfg.sm_scale, qblock_mask=mask, nthreads=nth)
+        t1 = time.perf_counter()
+        oracle.attn_bwd(orc["qp"], orc["kp"], vp, dop, orc["block_start"], orc["nblocks"], 1, orc["sel_count"],
+                        orc["sel_idx"], cfg.sm_scale, qblock_mask=mask,
+                        kblock_mask=np.zeros_like(mask), nthreads=nth)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        spent += t2 - t0
+        rounds += 1
+    # dK/dV visit the same query-key pairs with the same per-pair arithmetic as the
+    # row statistics + dQ pass, so the backward per pair is taken as twice that pass
+    per_pair = (t_fwd + 2.0 * t_bwd) / max(pairs_s, 1)
+    est_ms = (t_plan + per_pair * total) * 1e3
+    sample = (f"planning (stats, shapes, layout, permute+pool Q/K, full selection) timed in full "
+              f"({t_plan:.1f} s); attention fwd + row-stat/dQ timed on {rounds} x {nq} query blocks per head "
+              f"({pairs_s:,} of {total:,} query-key pairs, {spent:.1f} s), dK/dV taken equal to the dQ pass per "
+              f"pair, extrapolated by pairs")
+    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": nth, "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
+              f"described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_block_sparse_var_amd as P
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    log(f"bench: config {cfg.name} grid {cfg.T}x{cfg.H}x{cfg.W} heads {cfg.heads} d {cfg.d}; generating inputs")
+    inp = synth.make_inputs(cfg, with_dout=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(inp["q"]).to(dt).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dt).to(dev)
+    v = torch.from_numpy(inp["v"]).to(dt).to(dev)
+    do = torch.from_numpy(inp["dout"]).to(dt).to(dev)
+    a = torch.from_numpy(inp["a"]).to(dev)
+    pb = P.make_problem(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.groups, cfg.dtype)
+    L = P.PrismLayer(pb, device=dev, backward=True)
+    pb32 = P.Problem(pb.T, pb.H, pb.W, pb.heads, pb.head_dim, pb.groups, P.F32)
+    sm = cfg.sm_scale
+    stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
+              "permute_do", "bsa_bwd", "unpermute_grads"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        P.prism_zone_stats(pb, v, a, cfg.eps, L.g, L.rho, L.zone_audio)
+        mark(1)
+        P.prism_assign_shapes(pb, L.g, L.rho, cfg.tau128, cfg.tau256, L.shape_idx, L.zone_block_off, L.block_start)
+        mark(2)
+        P.prism_permute(pb, L.shape_idx, 0, [q, k, v], [L.qp, L.kp, L.vp])
+        mark(3)
+        P.prism_pool_blocks(pb, L.block_start, [L.qp, L.kp], [L.qbar, L.kbar])
+        mark(4)
+        P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, cfg.k_abs, cfg.k_frac, cfg.p, L.sel_count,
+                              L.sel_idx)
+        mark(5)
+        P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse)
+        mark(6)
+        P.prism_permute(pb, L.shape_idx, 1, [L.op], [L.o])
+        mark(7)
+        P.prism_permute(pb, L.shape_idx, 0, [do], [L.dop])
+        mark(8)
+        P.prism_bsa_bwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.dop, L.lse,
+                        L.dqp, L.dkp, L.dvp, L.workspace)
+        mark(9)
+        P.prism_permute(pb32, L.shape_idx, 1, [L.dqp, L.dkp, L.dvp], [L.dq, L.dk, L.dv])
+        mark(10)
+
+    if args.copy_probe_mb > 0:
+        src = torch.ones(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel events recorded by the library around its own launches
+    kev = {kn: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)] for kn in MFMA_KERNELS + HBM_KERNELS}
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(args.steps)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for st in range(args.steps):  # make every event a live HIP event before timing
+        for kn in kev:
+            for e in kev[kn][st]:
+                e.record()
+        for e in sev[st]:
+            e.record()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    t_start.record()
+    for st in range(args.steps):
+        for kn in kev:
+            P.prism_trace_kernel(kn, *kev[kn][st])
+        step(sev[st])
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    P.prism_trace_kernel(None)
+    ms_step = t_start.elapsed_time(t_stop) / args.steps
+
+    stage_ms = {s: sum(sev[st][i].elapsed_time(sev[st][i + 1]) for st in range(args.steps)) / args.steps
+                for i, s in enumerate(stages)}
+    kern_ms = {kn: sum(a_.elapsed_time(b_) for a_, b_ in kev[kn]) / args.steps for kn in kev}
+
+    pairs, key_frac, hist, nblocks = selection_stats(L, pb)
+    d = cfg.d
+    f_fwd = 4.0 * d * pairs
+    f_bwd = 2.5 * f_fwd
+    attn_ms = stage_ms["bsa_fwd"] + stage_ms["bsa_bwd"]
+    attn_tflops = (f_fwd + f_bwd) / (attn_ms * 1e-3) / 1e12
+    # algorithmic FLOPs per kernel: forward QK^T + PV; dK/dV kernel S, dP, dV, dK; dQ kernel
+    # only its dQ product (its S and dP are recomputation beyond the five backward GEMMs)
+    kflops = {"k_fwd": 4.0 * d * pairs, "k_dkdv": 8.0 * d * pairs, "k_dq": 2.0 * d * pairs}
+    N, H_ = cfg.N, cfg.heads
+    ebytes = 2 if cfg.dtype == "bf16" else 4
+    kbytes = {
+        "k_zone_stats": N * H_ * d * ebytes + 4 * N,
+        "k_pool": 2 * N * H_ * d * ebytes + 2 * H_ * pb.nbmax * d * 4,
+    }
+    dom = max(MFMA_KERNELS, key=lambda kn: kern_ms[kn])
+    achieved = kflops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    tr_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tr_path):
+        with open(tr_path) as f:
+            tr = json.load(f)
+        ent = tr.get(dom)
+        if ent and ent.get("source_sha") == kernel_source_sha() and ent.get("config") == cfg.name:
+            roof["traffic"] = ent["bytes_per_launch"]
+    # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
+    kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
+    kern_ms["k_permute"] = stage_ms["permute_qkv"]
+    hbm = {kn: {"ms": round(kern_ms[kn], 4), "GB/s": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9, 1),
+                "frac": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+           for kn in ("k_zone_stats", "k_permute", "k_pool")}
+
+    out = {
+        "metric": "2K-shaped sparse-attn fwd+bwd ms/layer, TFLOP/s and % bf16 MFMA peak",
+        "value": round(ms_step, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded generator; 2K-shaped token grid)",
+        "config": {"workload": f"{cfg.name}: {cfg.T}x{cfg.H}x{cfg.W} tokens, {cfg.heads} heads, d {cfg.d}, "
+                               f"k {cfg.k_frac:.0%} p {cfg.p}, forward + backward",
+                   "parallelism": "none (1 GPU)"},
+        "attn_fwd_bwd_ms": round(attn_ms, 3),
+        "attn_tflops": round(attn_tflops, 1),
+        "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
+        "kernel_ms": {kn: round(kern_ms[kn], 4) for kn in MFMA_KERNELS},
+        "hbm_stages": hbm,
+        "selection": {"executed_pairs": pairs, "mean_key_fraction": round(key_frac, 4), "n_blocks": nblocks,
+                      "zones_by_volume": {str(kk): vv for kk, vv in hist.items()}},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(inp, budget_s=args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

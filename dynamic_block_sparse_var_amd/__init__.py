@@ -87,6 +87,7 @@ def lib():
         "prism_select_blocks": (_i32, [_PB, _vp, _vp, _vp, _f32, _i32, _f64, _f64, _vp, _vp, _vp]),
         "prism_bsa_fwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "prism_bsa_bwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
+        "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
     }
@@ -179,6 +180,19 @@ def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_l
     _check(lib().prism_bsa_bwd(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale, _p(q), _p(k),
                                _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv), _p(workspace),
                                nbytes, _stream(stream)), "prism_bsa_bwd")
+
+
+def prism_trace_kernel(kernel, start_event=None, stop_event=None):
+    """Time one library kernel with two torch.cuda.Event(enable_timing=True) objects
+    (kernel=None clears all hooks).  The events must already exist as HIP events, so they
+    are recorded once here before their handles are handed over."""
+    if kernel is None:
+        _check(lib().prism_trace_kernel(None, None, None), "prism_trace_kernel")
+        return
+    for ev in (start_event, stop_event):
+        ev.record()
+    _check(lib().prism_trace_kernel(kernel.encode(), ctypes.c_void_p(start_event.cuda_event),
+                                    ctypes.c_void_p(stop_event.cuda_event)), "prism_trace_kernel")
 
 
 # ---- one layer -------------------------------------------------------------------------

@@ -29,6 +29,28 @@ prism_status check_hip(hipError_t e, const char* what) {
 
 prism_status check_launch(const char* what) { return check_hip(hipGetLastError(), what); }
 
+namespace {
+struct TraceSlot {
+  char name[32];
+  hipEvent_t start, stop;
+};
+TraceSlot g_trace[8];
+int g_trace_n = 0;
+}  // namespace
+
+KernelTrace::KernelTrace(const char* kernel, hipStream_t st) : st_(st) {
+  for (int i = 0; i < g_trace_n; ++i)
+    if (strcmp(g_trace[i].name, kernel) == 0) {
+      hipEventRecord(g_trace[i].start, st);
+      stop_ = g_trace[i].stop;
+      return;
+    }
+}
+
+KernelTrace::~KernelTrace() {
+  if (stop_) hipEventRecord(stop_, st_);
+}
+
 prism_status need_ptr(const void* p, const char* name) {
   return p ? PRISM_OK : fail(PRISM_E_NULL, "%s is NULL", name);
 }
@@ -99,6 +121,27 @@ const char* prism_status_string(prism_status s) {
 }
 
 const char* prism_last_error(void) { return g_err; }
+
+prism_status prism_trace_kernel(const char* kernel, void* start_event, void* stop_event) {
+  g_err[0] = 0;
+  if (!kernel) {
+    g_trace_n = 0;
+    return PRISM_OK;
+  }
+  if (!start_event || !stop_event) return fail(PRISM_E_NULL, "trace events are NULL");
+  if (strlen(kernel) >= sizeof(g_trace[0].name)) return fail(PRISM_E_RANGE, "kernel name too long");
+  int slot = -1;
+  for (int i = 0; i < g_trace_n; ++i)
+    if (strcmp(g_trace[i].name, kernel) == 0) slot = i;
+  if (slot < 0) {
+    if (g_trace_n >= 8) return fail(PRISM_E_RANGE, "all 8 trace slots in use");
+    slot = g_trace_n++;
+    strcpy(g_trace[slot].name, kernel);
+  }
+  g_trace[slot].start = static_cast<hipEvent_t>(start_event);
+  g_trace[slot].stop = static_cast<hipEvent_t>(stop_event);
+  return PRISM_OK;
+}
 
 int32_t prism_shape_table(int32_t* edges) {
   if (!edges) return 0;

@@ -527,6 +527,7 @@ prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cn
                              hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
+  KernelTrace tr("k_fwd", st);
   if (g.d == 64)
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
@@ -544,6 +545,8 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
                              hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
+  {
+  KernelTrace tr("k_dq", st);
   if (g.d == 64) {
     hipLaunchKernelGGL(k_dq<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N,
@@ -553,8 +556,10 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
                        (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax,
                        g.hpg, (int)g.N, scale2, sm_scale);
   }
+  }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
+  KernelTrace tr("k_dkdv", st);
   if (g.d == 64) {
     hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs,

@@ -134,6 +134,7 @@ prism_status launch_permute(const Geom& g, const uint8_t* shape_idx, int inverse
   }
   const int rowbytes = g.d * g.esize;
   dim3 grid(g.Z, g.heads, count);
+  KernelTrace tr("k_permute", st);
   switch (rowbytes / 16) {
     case 8:
       hipLaunchKernelGGL(k_permute<3>, grid, dim3(256), 0, st, pp, shape_idx, inverse, g.H, g.W, g.ZH, g.ZW, g.Z,
@@ -159,6 +160,7 @@ prism_status launch_pool(const Geom& g, const int32_t* block_start, int count, c
     pp.xbar[i] = xbar[i];
   }
   dim3 grid(g.nbmax, g.heads, count);
+  KernelTrace tr("k_pool", st);
   if (g.bf16) {
     if (g.d == 64)
       hipLaunchKernelGGL((k_pool<true, 64>), grid, dim3(256), 0, st, pp, block_start, g.nbmax, g.hpg, g.N);

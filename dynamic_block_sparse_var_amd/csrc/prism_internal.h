@@ -27,6 +27,18 @@ prism_status fail(prism_status s, const char* fmt, ...);
 prism_status check_hip(hipError_t e, const char* what);
 prism_status check_launch(const char* what);
 
+// Measurement hook (prism_trace_kernel): records the caller's events around one launch of the
+// named kernel if a hook is set for it.  Construct right before the launch.
+class KernelTrace {
+ public:
+  KernelTrace(const char* kernel, hipStream_t st);
+  ~KernelTrace();
+
+ private:
+  hipEvent_t stop_ = nullptr;
+  hipStream_t st_;
+};
+
 // Host-side validation helpers (no HIP calls).
 prism_status validate_problem(const prism_problem* pb);
 prism_status need_ptr(const void* p, const char* name);

@@ -209,13 +209,17 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
   if (g.nbmax > kSelMaxKeys)
     return fail(PRISM_E_SHAPE, "%d blocks exceed the selection capacity of %d", g.nbmax, kSelMaxKeys);
   const int tiles = (g.nbmax + 63) / 64;
+  {
+  KernelTrace tr("k_scores", st);
   hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, g.heads), dim3(256), 0, st, qbar, kbar,
                      reinterpret_cast<float*>(sel_idx), block_start, g.nbmax, g.hpg, g.d, (int)g.N, sm_scale);
+  }
   prism_status s = check_launch("k_scores");
   if (s != PRISM_OK) return s;
   int P2 = 1;
   while (P2 < g.nbmax) P2 <<= 1;
   const size_t lds = (size_t)P2 * sizeof(uint64_t);
+  KernelTrace tr("k_select", st);
   hipLaunchKernelGGL(k_select, dim3(g.nbmax, g.heads), dim3(1024), lds, st, sel_idx, sel_count, block_start, g.nbmax,
                      g.hpg, (int)g.N, k_abs, k_frac, (float)p);
   return check_launch("k_select");

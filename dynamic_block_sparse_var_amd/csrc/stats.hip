@@ -260,12 +260,15 @@ __global__ __launch_bounds__(1024) void k_assign_shapes(const float* __restrict_
 prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, float eps, float* gout, float* rho,
                                float* zone_audio, hipStream_t st) {
   dim3 grid(g.Z, g.groups);
+  {
+  KernelTrace tr("k_zone_stats", st);
   if (g.bf16)
     hipLaunchKernelGGL(k_zone_stats<true>, grid, dim3(256), 0, st, v, a, gout, rho, zone_audio, g.H, g.W, g.ZH,
                        g.ZW, g.Z, g.heads, g.d, g.hpg);
   else
     hipLaunchKernelGGL(k_zone_stats<false>, grid, dim3(256), 0, st, v, a, gout, rho, zone_audio, g.H, g.W, g.ZH,
                        g.ZW, g.Z, g.heads, g.d, g.hpg);
+  }
   prism_status s = check_launch("k_zone_stats");
   if (s != PRISM_OK) return s;
   hipLaunchKernelGGL(k_zone_finish, dim3(1), dim3(1024), 0, st, gout, zone_audio, a != nullptr ? 1 : 0, g.Z,
@@ -276,6 +279,7 @@ prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, flo
 prism_status launch_assign_shapes(const Geom& g, const float* gin, const float* rho, float tau128, float tau256,
                                   uint8_t* shape_idx, int32_t* zone_block_off, int32_t* block_start,
                                   hipStream_t st) {
+  KernelTrace tr("k_assign_shapes", st);
   hipLaunchKernelGGL(k_assign_shapes, dim3(g.groups), dim3(1024), 0, st, gin, rho, tau128, tau256, shape_idx,
                      zone_block_off, block_start, g.Z, g.nbmax, (int)g.N);
   return check_launch("k_assign_shapes");

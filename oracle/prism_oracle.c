@@ -329,7 +329,7 @@ int orc_pool(int heads, int groups, int N, int d, int nbmax, const int32_t* bloc
 /* ------------------------------------------------------------------------------------ */
 /* RG M3: hybrid Top-k / Top-p selection                                                  */
 
-typedef struct { double p; int32_t j; } pj_t;
+typedef struct { double p; double s; int32_t j; } pj_t;
 
 static int cmp_desc(const void* A, const void* B) {
   const pj_t* a = (const pj_t*)A;
@@ -377,6 +377,7 @@ static void select_task(void* vctx, int64_t task) {
     double s = 0;
     for (int e = 0; e < c->d; ++e) s += qi[e] * kj[e];
     pj[j].p = c->sm_scale * s;
+    pj[j].s = pj[j].p;
     pj[j].j = j;
     if (pj[j].p > mx) mx = pj[j].p;
   }
@@ -409,7 +410,8 @@ static void select_task(void* vctx, int64_t task) {
   inf[0] = (double)kk;
   inf[1] = (double)np;
   inf[2] = (double)nsel;
-  inf[3] = (nsel < nb) ? (pj[nsel - 1].p - pj[nsel].p) / pj[nsel - 1].p : INFINITY;
+  /* order margin at the cut: relative gap of the block scores on either side of it */
+  inf[3] = (nsel < nb) ? (pj[nsel - 1].s - pj[nsel].s) / fmax(fabs(pj[nsel - 1].s), 1e-300) : INFINITY;
   if (c->p > 0 && np >= kk && np <= nb) {
     /* C_{n_p - 1} and C_{n_p} against p */
     double Cn = 0;

@@ -81,7 +81,8 @@ int orc_pool(int heads, int groups, int N, int d, int nbmax,
  * row_mask [heads,NBMAX] (NULL = all rows) restricts the work.
  * Outputs: sel_count [heads,NBMAX], sel_idx [heads,NBMAX,NBMAX] (row stride NBMAX),
  * info [heads,NBMAX,5] = {k, n_p, n_sel, order margin, cdf margin} (margins: relative gap
- * P_(n)-P_(n+1) at n = n_sel, and min |C_n - p|/p over n in {n_p-1, n_p} when n_p >= k;
+ * of the block scores (s_(n) - s_(n+1)) / |s_(n)| at the cut n = n_sel, and
+ * min |C_n - p|/p over n in {n_p-1, n_p} when n_p >= k;
  * +inf where not applicable). */
 int orc_select(int heads, int groups, int d, int nbmax, const int32_t* nblocks,
                const double* qbar, const double* kbar, double sm_scale,

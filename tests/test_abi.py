@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert P.prism_abi_version() == 1
