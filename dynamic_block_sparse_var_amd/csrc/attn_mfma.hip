@@ -74,10 +74,18 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Transposed tiles are 64 elements (128 bytes) wide.  The eight 16-byte granules of row d are
+// stored XOR-swizzled by (d/8 + d) mod 8: the 8 rows a group of 8 lanes reads in one
+// ds_read_b128 (consecutive d) then cover all 32 banks, and the writers (rows 8 apart) collide
+// at most pairwise.  toff(d, p) = element offset of position p (p % 8 == 0 for reads).
+__device__ __forceinline__ int toff(int d, int p) {
+  return d * 64 + ((((p >> 3) ^ ((d >> 3) + d)) & 7) << 3) + (p & 7);
+}
+
 template <int D>
 struct Cfg {
   static constexpr int KP = D + 8;          // row-major tile pitch, elements (2*D + 16 bytes)
-  static constexpr int TP = 64 + 8;         // transposed tile pitch, elements (144 bytes)
+  static constexpr int TP = 64;             // transposed tile pitch, elements (swizzled, see toff)
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
   static constexpr int QPP = 128 / CPR;     // 4-row quads per pass of 128 threads
   static constexpr int NP = D / 64;         // passes per 64-row tile (16 quads)
@@ -129,7 +137,7 @@ __device__ __forceinline__ void lstore_trans(uint16_t* s, const u32x4 (&r)[Cfg<D
         out[0] = (r[it][0][wd] & 0xffffu) | (r[it][1][wd] << 16);
         out[1] = (r[it][2][wd] & 0xffffu) | (r[it][3][wd] << 16);
       }
-      *reinterpret_cast<u32x2*>(s + (8 * c + i) * Cfg<D>::TP + col) = out;
+      *reinterpret_cast<u32x2*>(s + toff(8 * c + i, col)) = out;
     }
   }
 }
@@ -256,7 +264,7 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
       pack8_split(sacc[t >> 1], 8 * (t & 1), p_hi, p_lo);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vt_op = as_bf16x8(lds16(sVt + (32 * db + l32) * C::TP + 16 * t + 8 * half));
+        const bf16x8 vt_op = as_bf16x8(lds16(sVt + toff(32 * db + l32, 16 * t + 8 * half)));
         oacc[db] = mfma(vt_op, p_hi, oacc[db]);
         oacc[db] = mfma(vt_op, p_lo, oacc[db]);
       }
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, c
           const int t = 2 * kb + tt;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const bf16x8 kt_op = as_bf16x8(lds16(sKt + (32 * db + l32) * C::TP + 16 * t + 8 * half));
+            const bf16x8 kt_op = as_bf16x8(lds16(sKt + toff(32 * db + l32, 16 * t + 8 * half)));
             dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
             dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
           }
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q,
             pack8_split(dpacc, 8 * t, da_hi, da_lo);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const int off = (32 * db + l32) * C::TP + 32 * rb + 16 * t + 8 * half;
+              const int off = toff(32 * db + l32, 32 * rb + 16 * t + 8 * half);
               const bf16x8 dot_op = as_bf16x8(lds16(sdOt + off));
               const bf16x8 qt_op = as_bf16x8(lds16(sQt + off));
               dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
