@@ -3,27 +3,34 @@
 //
 // Work decomposition.  Every block holds 64, 128 or 256 rows and starts on a multiple of 64,
 // so the unit of work is a 64-row "atom" of one head.  A workgroup is two wave64s; each wave
-// owns 32 rows of the atom.  Key (or query) tiles of 64 rows are staged in LDS once per
-// workgroup and shared by both waves.  Atoms are assigned so that each of the 8 XCDs walks a
-// contiguous range of atoms (neighbouring blocks tend to select the same key blocks, which
-// then stay in that XCD's L2).
+// owns 32 rows (or 32 keys) of the atom.  The other operand is streamed in 64-row tiles that
+// are staged once per workgroup in LDS, row-major, and shared by both waves; the next tile's
+// global loads are issued before the current tile is computed (register double buffering).
+// Atoms are assigned so that each of the 8 XCDs walks a contiguous range of atoms
+// (neighbouring blocks tend to select the same key blocks, which then stay in that XCD's L2).
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16): operand A holds A[m = lane%32][8 k-values],
 // operand B holds B[8 k-values][n = lane%32]; both use lane/32 to pick which half of the 16
 // k-slots they hold.  The accumulator holds C[m = 8*jj + 4*(lane/32) + e][n = lane%32] in
-// element 4*jj + e.  Reductions over the head dimension read 8 consecutive elements of a
-// row-major tile (the k-slot -> d map just has to agree between A and B).  Reductions over
-// keys or query rows read a transposed tile whose 64-wide rows store row index r at
-// position tpos(r) (bits 2 and 3 swapped), which makes the 8 rows an accumulator lane holds
-// for one k-step contiguous, so the accumulator itself is the next product's B (or A)
-// operand after conversion to bf16.
+// element 4*jj + e.
+//  - Reductions over the head dimension read 8 consecutive elements of a tile row with one
+//    ds_read_b128 (the k-slot -> d map only has to agree between A and B).
+//  - Reductions over keys or query rows need, per lane, 8 rows of one column.  A lane's
+//    accumulator holds rows {8*jj + 4*h + e}; for k-step t the slots are mapped to rows
+//    16t + 8*(e/4) + 4*h + e%4, so the accumulator converted to bf16 is directly the B (or A)
+//    operand of the next product, and the other operand is read from the row-major tile with
+//    two ds_read_b64_tr_b16 (gfx950 transposing LDS read: within each 16-lane group, lane i
+//    receives element i%4 of the 8-byte reads of lanes 4e + i/4, e = 0..3).
 //
-// Forward:  S^T = K Q^T (A = K tile, B = Q rows kept in registers), online softmax per query
-//           row (each lane owns one row, the other 32 keys of the tile sit in lane ^ 32),
-//           O^T += V^T P^T (A = transposed V tile, B = P^T straight from the accumulator).
+// Forward:  S^T = K Q^T (A = K tile, B = Q rows in registers), online softmax per query row
+//           (each lane owns one row; the other 32 keys of a tile sit in lane ^ 32; the
+//           running max is only raised when a tile exceeds it by 2^8, so the O rescale is
+//           rare), O^T += V^T P^T with P split into a bf16 head and residual.
 // dQ:       S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - delta), dQ^T += K^T dS^T.
 // dK, dV:   key-major: for every query block whose list contains the key block (transposed
 //           selection bitmap), S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q.
+// Products with P and dS use a bf16 head plus a bf16 residual of the fp32 value, so the
+// results keep fp32-level accuracy.
 #include <math.h>
 
 #include "attn_common.h"
@@ -37,9 +44,12 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -47,15 +57,7 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 accumulator elements [off, off + 8) -> bf16 operand (round to nearest even)
-__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int off) {
-  f32x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = x[off + i];
-  return __builtin_convertvector(v, bf16x8);
-}
-
-// the same 8 elements as a bf16 head plus a bf16 residual: hi + lo carries ~16 significant bits
+// 8 accumulator elements [off, off + 8) as a bf16 head plus a bf16 residual
 __device__ __forceinline__ void pack8_split(const f32x16& x, int off, bf16x8& hi, bf16x8& lo) {
   f32x8 v;
 #pragma unroll
@@ -72,77 +74,56 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-__device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Transposed tiles are 64 elements (128 bytes) wide.  The eight 16-byte granules of row d are
-// stored XOR-swizzled by (d/8 + d) mod 8: the 8 rows a group of 8 lanes reads in one
-// ds_read_b128 (consecutive d) then cover all 32 banks, and the writers (rows 8 apart) collide
-// at most pairwise.  toff(d, p) = element offset of position p (p % 8 == 0 for reads).
-__device__ __forceinline__ int toff(int d, int p) {
-  return d * 64 + ((((p >> 3) ^ ((d >> 3) + d)) & 7) << 3) + (p & 7);
-}
-
 template <int D>
 struct Cfg {
   static constexpr int KP = D + 8;          // row-major tile pitch, elements (2*D + 16 bytes)
-  static constexpr int TP = 64;             // transposed tile pitch, elements (swizzled, see toff)
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int QPP = 128 / CPR;     // 4-row quads per pass of 128 threads
-  static constexpr int NP = D / 64;         // passes per 64-row tile (16 quads)
-  static constexpr int RPP = 128 / CPR;     // rows per pass (epilogue copy)
+  static constexpr int RPP = 128 / CPR;     // rows per pass of 128 threads
+  static constexpr int NIT = 64 / RPP;      // 16-byte loads per thread for a 64-row tile
   static constexpr int DS = D / 16;         // k-steps over the head dimension
   static constexpr int DB = D / 32;         // 32-wide blocks of the head dimension
+  static constexpr int TILE = 64 * KP;      // elements of one staged tile
 };
 
-// global -> registers: thread t takes chunk t % CPR of rows 4q..4q+3 for quads q = t/CPR + QPP*it
+// global -> registers: thread t takes chunk t % CPR of rows t / CPR + RPP * it
 template <int D>
-__device__ __forceinline__ void gload_quads(const uint16_t* __restrict__ base, u32x4 (&r)[Cfg<D>::NP][4], int tid) {
-  const int c = tid % Cfg<D>::CPR, q0 = tid / Cfg<D>::CPR;
+__device__ __forceinline__ void gload(const uint16_t* __restrict__ base, u32x4 (&r)[Cfg<D>::NIT], int tid) {
+  const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
 #pragma unroll
-  for (int it = 0; it < Cfg<D>::NP; ++it) {
-    const int q = q0 + Cfg<D>::QPP * it;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r[it][e] = *reinterpret_cast<const u32x4*>(base + (int64_t)(4 * q + e) * D + 8 * c);
-  }
+  for (int it = 0; it < Cfg<D>::NIT; ++it)
+    r[it] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + Cfg<D>::RPP * it) * D + 8 * c);
 }
 
 template <int D>
-__device__ __forceinline__ void lstore_rows(uint16_t* s, const u32x4 (&r)[Cfg<D>::NP][4], int tid) {
-  const int c = tid % Cfg<D>::CPR, q0 = tid / Cfg<D>::CPR;
+__device__ __forceinline__ void lstore(uint16_t* s, const u32x4 (&r)[Cfg<D>::NIT], int tid) {
+  const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
 #pragma unroll
-  for (int it = 0; it < Cfg<D>::NP; ++it) {
-    const int q = q0 + Cfg<D>::QPP * it;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(s + (4 * q + e) * Cfg<D>::KP + 8 * c) = r[it][e];
-  }
-}
-
-// transposed store: element i of the 4 rows of a quad -> 4 consecutive positions of row 8c+i
-template <int D>
-__device__ __forceinline__ void lstore_trans(uint16_t* s, const u32x4 (&r)[Cfg<D>::NP][4], int tid) {
-  const int c = tid % Cfg<D>::CPR, q0 = tid / Cfg<D>::CPR;
-#pragma unroll
-  for (int it = 0; it < Cfg<D>::NP; ++it) {
-    const int q = q0 + Cfg<D>::QPP * it;
-    const int col = tpos(4 * q);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int wd = i >> 1;
-      u32x2 out;
-      if (i & 1) {
-        out[0] = (r[it][0][wd] >> 16) | (r[it][1][wd] & 0xffff0000u);
-        out[1] = (r[it][2][wd] >> 16) | (r[it][3][wd] & 0xffff0000u);
-      } else {
-        out[0] = (r[it][0][wd] & 0xffffu) | (r[it][1][wd] << 16);
-        out[1] = (r[it][2][wd] & 0xffffu) | (r[it][3][wd] << 16);
-      }
-      *reinterpret_cast<u32x2*>(s + toff(8 * c + i, col)) = out;
-    }
-  }
+  for (int it = 0; it < Cfg<D>::NIT; ++it)
+    *reinterpret_cast<u32x4*>(s + (r0 + Cfg<D>::RPP * it) * Cfg<D>::KP + 8 * c) = r[it];
 }
 
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
+// Operand holding X[R0 + 8*(e/4) + 4*(lane/32) + e%4][D0 + lane%32], e = 0..7, of a row-major
+// tile X (pitch KP) -- the lane's 8 k-slots when the product reduces over rows.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_rows_operand(const uint16_t* s, int R0, int D0, int lane) {
+  const int j = lane & 15;
+  const int row = R0 + 4 * (lane >> 5) + (j >> 2);
+  const int col = D0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const u32x2 a = lds_tr(s + row * Cfg<D>::KP + col);
+  const u32x2 b = lds_tr(s + (row + 8) * Cfg<D>::KP + col);
+  u32x4 v;
+  v[0] = a[0];
+  v[1] = a[1];
+  v[2] = b[0];
+  v[3] = b[1];
+  return as_bf16x8(v);
+}
 
 // atoms of one head, spread so that each XCD (workgroup id mod 8) walks a contiguous range
 __device__ __forceinline__ int xcd_atom(int bid, int natoms) {
@@ -154,11 +135,77 @@ template <int D>
 __device__ __forceinline__ void copy_out(uint16_t* __restrict__ dst, const uint16_t* s, int tid) {
   const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
 #pragma unroll
-  for (int it = 0; it < 64 / Cfg<D>::RPP; ++it) {
+  for (int it = 0; it < Cfg<D>::NIT; ++it) {
     const int r = r0 + Cfg<D>::RPP * it;
     *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + 8 * c) = lds16(s + r * Cfg<D>::KP + 8 * c);
   }
 }
+
+// Walks the 64-row tiles of the key blocks in a selection list (wave-uniform state).
+struct ListTiles {
+  const int32_t* list;
+  const int32_t* bs;
+  int cnt, sidx, kt, kend;
+  __device__ void begin(const int32_t* l, const int32_t* b, int c) {
+    list = l;
+    bs = b;
+    cnt = c;
+    sidx = 0;
+    kt = kend = 0;
+    if (cnt > 0) {
+      const int j = list[0];
+      kt = bs[j];
+      kend = bs[j + 1];
+    }
+  }
+  __device__ bool valid() const { return sidx < cnt; }
+  __device__ void next() {
+    kt += 64;
+    if (kt >= kend) {
+      ++sidx;
+      if (sidx < cnt) {
+        const int j = list[sidx];
+        kt = bs[j];
+        kend = bs[j + 1];
+      }
+    }
+  }
+};
+
+// Walks the 64-row tiles of the query blocks whose bit is set in a transposed-selection row.
+struct MaskTiles {
+  const uint32_t* mrow;
+  const int32_t* bs;
+  int nw, wi, rt, rend;
+  uint32_t bits;
+  __device__ void advance_block() {
+    while (true) {
+      while (bits == 0u) {
+        if (++wi >= nw) return;
+        bits = mrow[wi];
+      }
+      const int qb = (wi << 5) + __ffs(bits) - 1;
+      bits &= bits - 1;
+      rt = bs[qb];
+      rend = bs[qb + 1];
+      return;
+    }
+  }
+  __device__ void begin(const uint32_t* m, const int32_t* b, int n) {
+    mrow = m;
+    bs = b;
+    nw = n;
+    wi = 0;
+    rt = rend = 0;
+    bits = (nw > 0) ? mrow[0] : 0u;
+    if (nw > 0) advance_block();
+  }
+  __device__ bool valid() const { return wi < nw; }
+  __device__ void next() {
+    rt += 64;
+    if (rt >= rend) advance_block();
+  }
+};
 
 // ------------------------------------------------------------------------------------------
 // forward
@@ -172,16 +219,14 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                 float scale2) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * C::TP];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[C::TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
   const int natoms = N >> 6;
   const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int qb = block_of_row(bs, nbmax, row0);
-  const int cnt = sel_count[(int64_t)h * nbmax + qb];
-  const int32_t* list = sel_idx + ((int64_t)h * nbmax + qb) * nbmax;
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
@@ -197,32 +242,22 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   for (int db = 0; db < C::DB; ++db) oacc[db] = zero16();
   float mrow = -INFINITY, lrow = 0.f;
 
-  u32x4 kreg[C::NP][4], vreg[C::NP][4];
-  int sidx = 0, kt = 0, kend = 0;
-  if (cnt > 0) {
-    const int j = list[0];
-    kt = bs[j];
-    kend = bs[j + 1];
-    gload_quads<D>(Kh + (int64_t)kt * D, kreg, tid);
-    gload_quads<D>(Vh + (int64_t)kt * D, vreg, tid);
+  ListTiles it;
+  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
+  u32x4 kreg[C::NIT], vreg[C::NIT];
+  if (it.valid()) {
+    gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
+    gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
   }
-  while (sidx < cnt) {
+  while (it.valid()) {
     __syncthreads();
-    lstore_rows<D>(sK, kreg, tid);
-    lstore_trans<D>(sVt, vreg, tid);
+    lstore<D>(sK, kreg, tid);
+    lstore<D>(sV, vreg, tid);
     __syncthreads();
-    int nkt = kt + 64, nsidx = sidx, nkend = kend;
-    if (nkt >= kend) {
-      ++nsidx;
-      if (nsidx < cnt) {
-        const int j = list[nsidx];
-        nkt = bs[j];
-        nkend = bs[j + 1];
-      }
-    }
-    if (nsidx < cnt) {
-      gload_quads<D>(Kh + (int64_t)nkt * D, kreg, tid);
-      gload_quads<D>(Vh + (int64_t)nkt * D, vreg, tid);
+    it.next();
+    if (it.valid()) {
+      gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
+      gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
     }
     // S^T = K Q^T for this wave's 32 rows
     f32x16 sacc[2];
@@ -233,45 +268,44 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
 #pragma unroll
       for (int s = 0; s < C::DS; ++s) sacc[kb] = mfma(as_bf16x8(lds16(ka + 8 * s)), qop[s], sacc[kb]);
     }
-    // online softmax (base 2, logits scaled by sm_scale * log2 e)
+    // online softmax in base 2 (logits scaled by sm_scale * log2 e); the running max is
+    // raised (and O rescaled) only when this tile exceeds it by more than the slack
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx * scale2);
-    const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+    if (__any(mx > mrow + kRescaleSlack)) {
+      const float mnew = fmaxf(mrow, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      lrow *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      mrow = mnew;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], scale2, -mnew));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], scale2, -mrow));
         sacc[kb][r] = pv;
         psum += pv;
       }
-    psum += __shfl_xor(psum, 32, 64);
-    lrow = fmaf(lrow, alpha, psum);
-    mrow = mnew;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-    // O^T += V^T P^T, with P as bf16 head + residual so O keeps fp32-level accuracy (the
-    // backward's delta = dO . O cancels against dP and would expose bf16 rounding of P)
+    lrow += psum + __shfl_xor(psum, 32, 64);
+    // O^T += V^T P^T, P as bf16 head + residual
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bf16x8 p_hi, p_lo;
       pack8_split(sacc[t >> 1], 8 * (t & 1), p_hi, p_lo);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vt_op = as_bf16x8(lds16(sVt + toff(32 * db + l32, 16 * t + 8 * half)));
+        const bf16x8 vt_op = lds_rows_operand<D>(sV, 16 * t, 32 * db, lane);
         oacc[db] = mfma(vt_op, p_hi, oacc[db]);
         oacc[db] = mfma(vt_op, p_lo, oacc[db]);
       }
     }
-    kt = nkt;
-    sidx = nsidx;
-    kend = nkend;
   }
   const float inv = (lrow > 0.f) ? 1.f / lrow : 0.f;
   if (half == 0) LSE[(int64_t)h * N + row0 + 32 * w + l32] = (lrow > 0.f) ? (mrow + log2f(lrow)) * kLn2 : -INFINITY;
@@ -311,18 +345,17 @@ __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, c
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                float scale2, float sm_scale) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[64 * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * C::TP];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[C::TILE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
   const int natoms = N >> 6;
   const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int qb = block_of_row(bs, nbmax, row0);
-  const int cnt = sel_count[(int64_t)h * nbmax + qb];
-  const int32_t* list = sel_idx + ((int64_t)h * nbmax + qb) * nbmax;
   const int64_t hoff = (int64_t)h * N * D;
+  const uint16_t* Kh = K + hoff;
+  const uint16_t* Vh = V + hoff;
   const int myrow = row0 + 32 * w + l32;
 
   bf16x8 qop[C::DS], doop[C::DS];
@@ -341,45 +374,48 @@ __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, c
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqacc[db] = zero16();
 
-  for (int sidx = 0; sidx < cnt; ++sidx) {
-    const int j = list[sidx];
-    for (int kt = bs[j]; kt < bs[j + 1]; kt += 64) {
-      {
-        u32x4 kreg[C::NP][4], vreg[C::NP][4];
-        gload_quads<D>(K + hoff + (int64_t)kt * D, kreg, tid);
-        gload_quads<D>(V + hoff + (int64_t)kt * D, vreg, tid);
-        __syncthreads();
-        lstore_rows<D>(sK, kreg, tid);
-        lstore_trans<D>(sKt, kreg, tid);
-        lstore_rows<D>(sV, vreg, tid);
-        __syncthreads();
+  ListTiles it;
+  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
+  u32x4 kreg[C::NIT], vreg[C::NIT];
+  if (it.valid()) {
+    gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
+    gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
+  }
+  while (it.valid()) {
+    __syncthreads();
+    lstore<D>(sK, kreg, tid);
+    lstore<D>(sV, vreg, tid);
+    __syncthreads();
+    it.next();
+    if (it.valid()) {
+      gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
+      gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc = zero16(), dpacc = zero16();
+      const uint16_t* ka = sK + (32 * kb + l32) * C::KP + (D / 2) * half;
+      const uint16_t* va = sV + (32 * kb + l32) * C::KP + (D / 2) * half;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        sacc = mfma(as_bf16x8(lds16(ka + 8 * s)), qop[s], sacc);
+        dpacc = mfma(as_bf16x8(lds16(va + 8 * s)), doop[s], dpacc);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 sacc = zero16(), dpacc = zero16();
-        const uint16_t* ka = sK + (32 * kb + l32) * C::KP + (D / 2) * half;
-        const uint16_t* va = sV + (32 * kb + l32) * C::KP + (D / 2) * half;
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -lse2));
+        sacc[r] = pv * (dpacc[r] - dl);
+      }
 #pragma unroll
-        for (int s = 0; s < C::DS; ++s) {
-          sacc = mfma(as_bf16x8(lds16(ka + 8 * s)), qop[s], sacc);
-          dpacc = mfma(as_bf16x8(lds16(va + 8 * s)), doop[s], dpacc);
-        }
+      for (int tt = 0; tt < 2; ++tt) {
+        bf16x8 ds_hi, ds_lo;
+        pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
+        const int t = 2 * kb + tt;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -lse2));
-          sacc[r] = pv * (dpacc[r] - dl);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          bf16x8 ds_hi, ds_lo;
-          pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
-          const int t = 2 * kb + tt;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const bf16x8 kt_op = as_bf16x8(lds16(sKt + toff(32 * db + l32, 16 * t + 8 * half)));
-            dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
-            dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
-          }
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 kt_op = lds_rows_operand<D>(sK, 16 * t, 32 * db, lane);
+          dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
+          dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
         }
       }
     }
@@ -411,10 +447,8 @@ __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
                                                  int N, float scale2, float sm_scale) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[64 * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[64 * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * C::TP];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * C::TP];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[C::TILE];
   __shared__ __attribute__((aligned(16))) float sL[64];
   __shared__ __attribute__((aligned(16))) float sD[64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -423,7 +457,6 @@ __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q,
   const int key0 = xcd_atom(blockIdx.x, natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int kb_idx = block_of_row(bs, nbmax, key0);
-  const uint32_t* mrow = mask_t + ((int64_t)h * nbmax + kb_idx) * nw;
   const int64_t hoff = (int64_t)h * N * D;
   const int mykey = key0 + 32 * w + l32;
 
@@ -444,73 +477,68 @@ __global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q,
     dvacc[db] = zero16();
   }
 
-  for (int wi = 0; wi < nw; ++wi) {
-    uint32_t bits = mrow[wi];
-    while (bits) {
-      const int qbk = (wi << 5) + __ffs(bits) - 1;
-      bits &= bits - 1;
-      for (int rt = bs[qbk]; rt < bs[qbk + 1]; rt += 64) {
-        {
-          u32x4 qreg[C::NP][4], oreg[C::NP][4];
-          gload_quads<D>(Q + hoff + (int64_t)rt * D, qreg, tid);
-          gload_quads<D>(dO + hoff + (int64_t)rt * D, oreg, tid);
-          float lv = 0.f, dv = 0.f;
-          if (tid < 64) {
-            lv = LSE[(int64_t)h * N + rt + tid] * kLog2e;
-            dv = delta[(int64_t)h * N + rt + tid];
-          }
-          __syncthreads();
-          lstore_rows<D>(sQ, qreg, tid);
-          lstore_trans<D>(sQt, qreg, tid);
-          lstore_rows<D>(sdO, oreg, tid);
-          lstore_trans<D>(sdOt, oreg, tid);
-          if (tid < 64) {
-            sL[tid] = lv;
-            sD[tid] = dv;
-          }
-          __syncthreads();
+  MaskTiles it;
+  it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw);
+  u32x4 qreg[C::NIT], oreg[C::NIT];
+  float lv = 0.f, dv = 0.f;
+  auto prefetch = [&](int rt) {
+    gload<D>(Q + hoff + (int64_t)rt * D, qreg, tid);
+    gload<D>(dO + hoff + (int64_t)rt * D, oreg, tid);
+    if (tid < 64) {
+      lv = LSE[(int64_t)h * N + rt + tid] * kLog2e;
+      dv = delta[(int64_t)h * N + rt + tid];
+    }
+  };
+  if (it.valid()) prefetch(it.rt);
+  while (it.valid()) {
+    __syncthreads();
+    lstore<D>(sQ, qreg, tid);
+    lstore<D>(sdO, oreg, tid);
+    if (tid < 64) {
+      sL[tid] = lv;
+      sD[tid] = dv;
+    }
+    __syncthreads();
+    it.next();
+    if (it.valid()) prefetch(it.rt);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // S = Q K^T and dP = dO V^T for query rows 32rb.. of the tile, this wave's 32 keys
+      f32x16 sacc = zero16(), dpacc = zero16();
+      const uint16_t* qa = sQ + (32 * rb + l32) * C::KP + (D / 2) * half;
+      const uint16_t* oa = sdO + (32 * rb + l32) * C::KP + (D / 2) * half;
+#pragma unroll
+      for (int s = 0; s < C::DS; ++s) {
+        sacc = mfma(as_bf16x8(lds16(qa + 8 * s)), kop[s], sacc);
+        dpacc = mfma(as_bf16x8(lds16(oa + 8 * s)), vop[s], dpacc);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rr = 32 * rb + 8 * jj + 4 * half;
+        const float4 L4 = *reinterpret_cast<const float4*>(sL + rr);
+        const float4 D4 = *reinterpret_cast<const float4*>(sD + rr);
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * jj + e;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -Lv[e]));
+          sacc[r] = pv;
+          dpacc[r] = pv * (dpacc[r] - Dv[e]);
         }
+      }
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          // S = Q K^T and dP = dO V^T for query rows 32rb.. of the tile, this wave's 32 keys
-          f32x16 sacc = zero16(), dpacc = zero16();
-          const uint16_t* qa = sQ + (32 * rb + l32) * C::KP + (D / 2) * half;
-          const uint16_t* oa = sdO + (32 * rb + l32) * C::KP + (D / 2) * half;
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 pa_hi, pa_lo, da_hi, da_lo;
+        pack8_split(sacc, 8 * t, pa_hi, pa_lo);
+        pack8_split(dpacc, 8 * t, da_hi, da_lo);
 #pragma unroll
-          for (int s = 0; s < C::DS; ++s) {
-            sacc = mfma(as_bf16x8(lds16(qa + 8 * s)), kop[s], sacc);
-            dpacc = mfma(as_bf16x8(lds16(oa + 8 * s)), vop[s], dpacc);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int rr = 32 * rb + 8 * jj + 4 * half;
-            const float4 L4 = *reinterpret_cast<const float4*>(sL + rr);
-            const float4 D4 = *reinterpret_cast<const float4*>(sD + rr);
-            const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * jj + e;
-              const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -Lv[e]));
-              sacc[r] = pv;
-              dpacc[r] = pv * (dpacc[r] - Dv[e]);
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            bf16x8 pa_hi, pa_lo, da_hi, da_lo;
-            pack8_split(sacc, 8 * t, pa_hi, pa_lo);
-            pack8_split(dpacc, 8 * t, da_hi, da_lo);
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              const int off = toff(32 * db + l32, 32 * rb + 16 * t + 8 * half);
-              const bf16x8 dot_op = as_bf16x8(lds16(sdOt + off));
-              const bf16x8 qt_op = as_bf16x8(lds16(sQt + off));
-              dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
-              dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
-              dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
-              dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
-            }
-          }
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x8 dot_op = lds_rows_operand<D>(sdO, 32 * rb + 16 * t, 32 * db, lane);
+          const bf16x8 qt_op = lds_rows_operand<D>(sQ, 32 * rb + 16 * t, 32 * db, lane);
+          dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
+          dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
+          dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
+          dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
         }
       }
     }
@@ -554,29 +582,27 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   {
-  KernelTrace tr("k_dq", st);
-  if (g.d == 64) {
-    hipLaunchKernelGGL(k_dq<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, (int)g.N,
-                       scale2, sm_scale);
-  } else {
-    hipLaunchKernelGGL(k_dq<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax,
-                       g.hpg, (int)g.N, scale2, sm_scale);
-  }
+    KernelTrace tr("k_dq", st);
+    if (g.d == 64)
+      hipLaunchKernelGGL(k_dq<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                         (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
+                         (int)g.N, scale2, sm_scale);
+    else
+      hipLaunchKernelGGL(k_dq<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                         (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
+                         (int)g.N, scale2, sm_scale);
   }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
   KernelTrace tr("k_dkdv", st);
-  if (g.d == 64) {
+  if (g.d == 64)
     hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs,
-                       mask_t, g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale);
-  } else {
+                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw,
+                       g.hpg, (int)g.N, scale2, sm_scale);
+  else
     hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs,
-                       mask_t, g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale);
-  }
+                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw,
+                       g.hpg, (int)g.N, scale2, sm_scale);
   return check_launch("k_dkdv");
 }
 
