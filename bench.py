@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -134,6 +135,55 @@ def cpu_baseline(inp, budget_s=20.0):
     return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": nth, "kind": "oracle", "sample": sample}
 
 
+def write_traffic(d, probe_mb, config):
+    """HBM bytes per dispatch from two rocprofv3 --pmc runs.  The counters are scaled by what
+    they read for the known-size device copy (probe_mb MiB read and written) in the same run."""
+    import csv
+    import glob
+
+    def load(cnt):
+        fs = glob.glob(os.path.join(d, cnt, "**", "*counter_collection.csv"), recursive=True)
+        if len(fs) != 1:
+            raise SystemExit(f"expected one counter CSV under {d}/{cnt}, found {fs}")
+        out = []
+        with open(fs[0]) as f:
+            for r in csv.DictReader(f):
+                out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]) * 1024.0))
+        return out
+
+    fetch, write = load("FETCH_SIZE"), load("WRITE_SIZE")
+    probe = probe_mb << 20
+
+    def scale(rows):
+        big = max((b for n, _, b in rows if "copyBuffer" in n), default=0.0)
+        if big <= 0:
+            raise SystemExit("no device-copy dispatch found to calibrate the counter")
+        return probe / big
+
+    fs, ws = scale(fetch), scale(write)
+    res = {}
+    for (nf, gf, bf), (nw, gw, bw) in zip(fetch, write):
+        if nf != nw or gf != gw:
+            raise SystemExit("FETCH_SIZE and WRITE_SIZE runs dispatched different kernels")
+        if "copyBuffer" in nf:
+            continue
+        m = re.search(r"::(k_\w+)", nf)
+        base = m.group(1) if m else nf
+        e = res.setdefault(base, {"per_dispatch": []})
+        e["per_dispatch"].append({"grid": gf, "read": round(bf * fs), "write": round(bw * ws)})
+    for e in res.values():
+        pdl = e["per_dispatch"]
+        e["bytes_per_launch"] = round(sum(x["read"] + x["write"] for x in pdl) / len(pdl))
+        e["source_sha"] = kernel_source_sha()
+        e["config"] = config
+    meta = {"fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "probe_bytes": probe,
+            "note": "bytes = counter KiB x 1024 x scale; scale = probe bytes / counter bytes of the probe copy"}
+    out = {"_calibration": meta, **res}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: v.get("bytes_per_launch") for k, v in res.items()}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,7 +195,14 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="no GPU work: read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR/FETCH_SIZE and "
+                         "DIR/WRITE_SIZE (taken with --copy-probe-mb on this source tree) and write "
+                         "profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from, args.copy_probe_mb or 4096, args.config)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
               f"described in DESIGN.md but not built.", file=sys.stderr)
@@ -266,7 +323,7 @@ def main():
         with open(tr_path) as f:
             tr = json.load(f)
         ent = tr.get(dom)
-        if ent and ent.get("source_sha") == kernel_source_sha() and ent.get("config") == cfg.name:
+        if isinstance(ent, dict) and ent and ent.get("source_sha") == kernel_source_sha() and ent.get("config") == cfg.name:
             roof["traffic"] = ent["bytes_per_launch"]
     # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
     kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
