@@ -57,14 +57,30 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 accumulator elements [off, off + 8) as a bf16 head plus a bf16 residual
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one instruction (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  f32x2 v;
+  v[0] = a;
+  v[1] = b;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 8 accumulator elements [off, off + 8) as a bf16 head plus a bf16 residual (the residual
+// x - head is exact in fp32)
 __device__ __forceinline__ void pack8_split(const f32x16& x, int off, bf16x8& hi, bf16x8& lo) {
-  f32x8 v;
+  u32x4 H, Lo;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = x[off + i];
-  hi = __builtin_convertvector(v, bf16x8);
-  const f32x8 back = __builtin_convertvector(hi, f32x8);
-  lo = __builtin_convertvector(v - back, bf16x8);
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[off + 2 * i], b = x[off + 2 * i + 1];
+    const uint32_t h = cvt2(a, b);
+    H[i] = h;
+    Lo[i] = cvt2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+  }
+  hi = as_bf16x8(H);
+  lo = as_bf16x8(Lo);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
