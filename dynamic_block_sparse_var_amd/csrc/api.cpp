@@ -48,7 +48,7 @@ KernelTrace::KernelTrace(const char* kernel, hipStream_t st) : st_(st) {
 }
 
 KernelTrace::~KernelTrace() {
-  if (stop_) hipEventRecord(stop_, st_);
+  if (stop_) (void)hipEventRecord(stop_, st_);
 }
 
 prism_status need_ptr(const void* p, const char* name) {

@@ -188,11 +188,12 @@ __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, c
 }
 
 // delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step.  O = o + o_lo when the
-// forward stored its rounding residual.
+// forward stored its rounding residual.  Also lse2 = LSE * log2(e), the row statistic in the
+// base-2 units the matrix-core backward uses.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T* __restrict__ olo,
-                                               const T* __restrict__ dout, float* __restrict__ delta,
-                                               int64_t rows) {
+                                               const T* __restrict__ dout, const float* __restrict__ lse,
+                                               float* __restrict__ delta, float* __restrict__ lse2, int64_t rows) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int LPR = D / EPC;  // lanes per row (8..32)
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -221,7 +222,10 @@ __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T*
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * 1.4426950408889634f;
+  }
 }
 
 template <typename T, int D>
@@ -254,8 +258,9 @@ BwdWorkspace bwd_workspace_layout(const Geom& g) {
   BwdWorkspace w;
   w.nw = (g.nbmax + 31) / 32;
   w.delta_off = 0;
-  const size_t delta_bytes = (size_t)g.heads * g.N * sizeof(float);
-  w.mask_off = (delta_bytes + 255) & ~(size_t)255;
+  const size_t delta_bytes = ((size_t)g.heads * g.N * sizeof(float) + 255) & ~(size_t)255;
+  w.lse2_off = delta_bytes;
+  w.mask_off = 2 * delta_bytes;
   const size_t mask_words = (size_t)g.heads * g.nbmax * w.nw;
   w.mask_words = mask_words;
   w.total = w.mask_off + ((mask_words * sizeof(uint32_t) + 255) & ~(size_t)255);
@@ -278,6 +283,7 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
                             hipStream_t st) {
   const BwdWorkspace w = bwd_workspace_layout(g);
   float* delta = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.delta_off);
+  float* lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.lse2_off);
   uint32_t* mask_t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + w.mask_off);
   // transposed selection
   const int fill_blocks = (int)((w.mask_words + 255) / 256 < 4096 ? (w.mask_words + 255) / 256 : 4096);
@@ -296,21 +302,22 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   if (g.bf16) {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<uint16_t, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)o_lo, (const uint16_t*)dout, delta, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows);
     else
       hipLaunchKernelGGL((k_delta<uint16_t, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)o_lo, (const uint16_t*)dout, delta, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows);
   } else {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<float, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)nullptr, (const float*)dout, delta, rows);
+                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows);
     else
       hipLaunchKernelGGL((k_delta<float, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)nullptr, (const float*)dout, delta, rows);
+                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows);
   }
   s = check_launch("k_delta");
   if (s != PRISM_OK) return s;
-  if (g.bf16) return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
+  if (g.bf16)
+    return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse2, delta, mask_t, w.nw, dq, dk, dv, st);
   if (g.d == 64)
     return run_ref_bwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
   return run_ref_bwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);

@@ -5,10 +5,11 @@
 
 namespace prism {
 
-// Backward workspace: delta [heads, N] fp32, then the transposed selection bitmap
-// [heads, NBMAX, nw] uint32 (nw = ceil(NBMAX / 32)), each 256-byte aligned.
+// Backward workspace: delta [heads, N] fp32, lse2 = LSE * log2(e) [heads, N] fp32, then the
+// transposed selection bitmap [heads, NBMAX, nw] uint32 (nw = ceil(NBMAX / 32)), each 256-byte
+// aligned.
 struct BwdWorkspace {
-  size_t delta_off, mask_off, mask_words, total;
+  size_t delta_off, lse2_off, mask_off, mask_words, total;
   int nw;
 };
 BwdWorkspace bwd_workspace_layout(const Geom& g);
@@ -18,7 +19,7 @@ prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cn
                              float* lse, hipStream_t st);
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, const void* dout,
-                             const float* lse, const float* delta, const uint32_t* mask_t, int nw, float* dq,
+                             const float* lse2, const float* delta, const uint32_t* mask_t, int nw, float* dq,
                              float* dk, float* dv, hipStream_t st);
 
 }  // namespace prism

@@ -90,55 +90,10 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-template <int D>
-struct Cfg {
-  static constexpr int KP = D + 8;          // row-major tile pitch, elements (2*D + 16 bytes)
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int RPP = 128 / CPR;     // rows per pass of 128 threads
-  static constexpr int NIT = 64 / RPP;      // 16-byte loads per thread for a 64-row tile
-  static constexpr int DS = D / 16;         // k-steps over the head dimension
-  static constexpr int DB = D / 32;         // 32-wide blocks of the head dimension
-  static constexpr int TILE = 64 * KP;      // elements of one staged tile
-};
-
-// global -> registers: thread t takes chunk t % CPR of rows t / CPR + RPP * it
-template <int D>
-__device__ __forceinline__ void gload(const uint16_t* __restrict__ base, u32x4 (&r)[Cfg<D>::NIT], int tid) {
-  const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
-#pragma unroll
-  for (int it = 0; it < Cfg<D>::NIT; ++it)
-    r[it] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r0 + Cfg<D>::RPP * it) * D + 8 * c);
-}
-
-template <int D>
-__device__ __forceinline__ void lstore(uint16_t* s, const u32x4 (&r)[Cfg<D>::NIT], int tid) {
-  const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
-#pragma unroll
-  for (int it = 0; it < Cfg<D>::NIT; ++it)
-    *reinterpret_cast<u32x4*>(s + (r0 + Cfg<D>::RPP * it) * Cfg<D>::KP + 8 * c) = r[it];
-}
-
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 __device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
-}
-
-// Operand holding X[R0 + 8*(e/4) + 4*(lane/32) + e%4][D0 + lane%32], e = 0..7, of a row-major
-// tile X (pitch KP) -- the lane's 8 k-slots when the product reduces over rows.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_rows_operand(const uint16_t* s, int R0, int D0, int lane) {
-  const int j = lane & 15;
-  const int row = R0 + 4 * (lane >> 5) + (j >> 2);
-  const int col = D0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const u32x2 a = lds_tr(s + row * Cfg<D>::KP + col);
-  const u32x2 b = lds_tr(s + (row + 8) * Cfg<D>::KP + col);
-  u32x4 v;
-  v[0] = a[0];
-  v[1] = a[1];
-  v[2] = b[0];
-  v[3] = b[1];
-  return as_bf16x8(v);
 }
 
 // atoms of one head, spread so that each XCD (workgroup id mod 8) walks a contiguous range
@@ -146,15 +101,95 @@ __device__ __forceinline__ int xcd_atom(int bid, int natoms) {
   return ((natoms & 7) == 0) ? (bid & 7) * (natoms >> 3) + (bid >> 3) : bid;
 }
 
-// copy a staged 64 x D bf16 tile (pitch KP) to global rows
+// ---- swizzled, unpadded 64 x D tiles filled by direct global -> LDS loads -----------------
+//
+// Row r occupies 2*D contiguous bytes; its 16-byte chunk c sits in chunk slot c ^ swz(r).  The
+// swizzle makes both read patterns bank-conflict free: 16 consecutive rows at one chunk
+// (ds_read_b128 operands) and 4 consecutive rows x 4 consecutive chunks (ds_read_b64_tr_b16).
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
 template <int D>
-__device__ __forceinline__ void copy_out(uint16_t* __restrict__ dst, const uint16_t* s, int tid) {
-  const int c = tid % Cfg<D>::CPR, r0 = tid / Cfg<D>::CPR;
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;      // rows per 1 KB load
+  static constexpr int NI = 16 / RPI;       // 1 KB loads per wave per tile (4 waves)
+  static constexpr int ELEMS = 64 * D;
+};
+
+// Staging a 64-row tile: each of the 4 waves issues NI loads of 1 KB (global_load_lds_dwordx4,
+// one 16-byte chunk per lane).  The hardware puts lane l's chunk at byte 16*l after the wave's
+// LDS base, so the lane fetches the chunk whose swizzled slot that is; off[i] is its byte
+// offset from the start of the source rows.  Completion is awaited with dma_wait() before the
+// workgroup barrier.
+template <int D>
+__device__ __forceinline__ void dma_offsets(int w, int lane, uint32_t (&off)[Tile<D>::NI]) {
+  using TL = Tile<D>;
 #pragma unroll
-  for (int it = 0; it < Cfg<D>::NIT; ++it) {
-    const int r = r0 + Cfg<D>::RPP * it;
-    *reinterpret_cast<u32x4*>(dst + (int64_t)r * D + 8 * c) = lds16(s + r * Cfg<D>::KP + 8 * c);
+  for (int i = 0; i < TL::NI; ++i) {
+    const int r = (w * TL::NI + i) * TL::RPI + lane / TL::CPR;
+    off[i] = r * 2 * D + (((lane % TL::CPR) ^ swz<D>(r)) << 4);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint16_t* s, int w,
+                                         const uint32_t (&off)[Tile<D>::NI]) {
+  using TL = Tile<D>;
+#pragma unroll
+  for (int i = 0; i < TL::NI; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(src) + off[i]),
+                                     (lds_void*)(reinterpret_cast<char*>(s) + (w * TL::NI + i) * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Byte addresses.  A b128 read of chunk c of row r is at row_addr(r) ^ (c << 4).  The two
+// transposing reads of tile_rows_op at rows R0.. (R0 % 16 == 0) and columns D0.. (D0 % 32 == 0)
+// are at (tr[b] ^ (2 * D0)) + 2 * D * R0, tr[] being the lane's addresses for R0 = D0 = 0.
+template <int D>
+__device__ __forceinline__ uint32_t row_addr(int r) {
+  return r * 2 * D + (swz<D>(r) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ void tr_addr(int lane, uint32_t (&tr)[2]) {
+  const int j = lane & 15;
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int row = 4 * (lane >> 5) + (j >> 2) + 8 * b;
+    tr[b] = row * 2 * D + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint16_t* s, uint32_t byte) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s) + byte));
+}
+
+__device__ __forceinline__ u32x2 lds_tr_at(const uint16_t* s, uint32_t byte) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(reinterpret_cast<const char*>(s) + byte)));
+}
+
+// Operand holding X[R0 + 8*(e/4) + 4*(lane/32) + e%4][D0 + lane%32], e = 0..7, of a swizzled
+// tile X -- the lane's 8 k-slots when the product reduces over rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_rows_op(const uint16_t* s, const uint32_t (&tr)[2], int R0, int D0) {
+  const u32x2 a = lds_tr_at(s, (tr[0] ^ (2 * D0)) + 2 * D * R0);
+  const u32x2 b = lds_tr_at(s, (tr[1] ^ (2 * D0)) + 2 * D * R0);
+  u32x4 v;
+  v[0] = a[0];
+  v[1] = a[1];
+  v[2] = b[0];
+  v[3] = b[1];
+  return as_bf16x8(v);
 }
 
 // Walks the 64-row tiles of the key blocks in a selection list (wave-uniform state).
@@ -226,18 +261,25 @@ struct MaskTiles {
 // ------------------------------------------------------------------------------------------
 // forward
 
+// Workgroup = 4 waves on one 64-row atom.  Wave w owns query rows 32*(w&1).. of the atom and,
+// of every staged 64-key tile, keys 32*(w>>1)..; the two waves sharing a row half keep separate
+// online-softmax states that are merged once at the end.  Tiles are double-buffered: the loads
+// of tile i+1 are in flight while tile i is computed, with one barrier per tile.
 template <int D>
-__global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                 uint16_t* __restrict__ Olo, float* __restrict__ LSE,
                                                 const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                 float scale2) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[C::TILE];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  constexpr int T = 64 * D;
+  constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
+  constexpr uint32_t SB = 4 * T;  // bytes of one stage (K tile, V tile)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T];  // two stages
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = w & 1, kh = w >> 1;
   const int h = blockIdx.y;
   const int natoms = N >> 6;
   const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
@@ -246,124 +288,161 @@ __global__ __launch_bounds__(128, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
+  const int myrow = row0 + 32 * rh + l32;
 
-  bf16x8 qop[C::DS];
+  bf16x8 qop[DS];
   {
-    const uint16_t* qr = Q + hoff + (int64_t)(row0 + 32 * w + l32) * D + (D / 2) * half;
+    const uint16_t* qr = Q + hoff + (int64_t)myrow * D + (D / 2) * half;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 8 * s));
+    for (int s = 0; s < DS; ++s) qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 8 * s));
   }
-  f32x16 oacc[C::DB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) oacc[db] = zero16();
+  for (int db = 0; db < DB; ++db) oacc[db] = zero16();
   float mrow = -INFINITY, lrow = 0.f;
 
   ListTiles it;
   it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
-  u32x4 kreg[C::NIT], vreg[C::NIT];
-  if (it.valid()) {
-    gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
-    gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
-  }
-  while (it.valid()) {
-    __syncthreads();
-    lstore<D>(sK, kreg, tid);
-    lstore<D>(sV, vreg, tid);
-    __syncthreads();
-    it.next();
-    if (it.valid()) {
-      gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
-      gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
-    }
-    // S^T = K Q^T for this wave's 32 rows
-    f32x16 sacc[2];
+  uint32_t doff[Tile<D>::NI], tra[2];
+  dma_offsets<D>(w, lane, doff);
+  tr_addr<D>(lane, tra);
+  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
+  auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
+    uint16_t* s = smem + soff / 2;
+    dma_tile<D>(Kh + (int64_t)it.kt * D, s, w, doff);
+    dma_tile<D>(Vh + (int64_t)it.kt * D, s + T, w, doff);
+  };
+  auto compute = [&]() __attribute__((always_inline)) {
+    const uint16_t* sK = smem;
+    const uint16_t* sV = smem + T;
+    // S^T = K Q^T for this wave's 32 keys x 32 rows
+    f32x16 sacc = zero16();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = zero16();
-      const uint16_t* ka = sK + (32 * kb + l32) * C::KP + (D / 2) * half;
+    for (int st = 0; st < DS; ++st) sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qop[st], sacc);
+    // online softmax in base 2 (logits scaled by sm_scale * log2 e); the running max is raised
+    // (and O rescaled) only when this tile exceeds it by more than the slack
+    float mx = sacc[0];
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) sacc[kb] = mfma(as_bf16x8(lds16(ka + 8 * s)), qop[s], sacc[kb]);
-    }
-    // online softmax in base 2 (logits scaled by sm_scale * log2 e); the running max is
-    // raised (and O rescaled) only when this tile exceeds it by more than the slack
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
     if (__any(mx > mrow + kRescaleSlack)) {
       const float mnew = fmaxf(mrow, mx);
       const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
       lrow *= alpha;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       mrow = mnew;
     }
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], scale2, -mrow));
-        sacc[kb][r] = pv;
-        psum += pv;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -mrow));
+      sacc[r] = pv;
+      psum += pv;
+    }
     lrow += psum + __shfl_xor(psum, 32, 64);
     // O^T += V^T P^T, P as bf16 head + residual
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int tt = 0; tt < 2; ++tt) {
       bf16x8 p_hi, p_lo;
-      pack8_split(sacc[t >> 1], 8 * (t & 1), p_hi, p_lo);
+      pack8_split(sacc, 8 * tt, p_hi, p_lo);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vt_op = lds_rows_operand<D>(sV, 16 * t, 32 * db, lane);
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 vt_op = tile_rows_op<D>(sV, tra, 32 * kh + 16 * tt, 32 * db);
         oacc[db] = mfma(vt_op, p_hi, oacc[db]);
         oacc[db] = mfma(vt_op, p_lo, oacc[db]);
       }
     }
+  };
+  if (it.valid()) {
+    uint32_t soff = 0;
+    stage(0);
+    while (true) {
+      dma_wait();
+      __syncthreads();
+      it.next();
+      const bool more = it.valid();
+      if (more) stage(soff ^ SB);
+      compute();
+      if (!more) break;
+      soff ^= SB;
+      rowa ^= SB;
+      tra[0] ^= SB;
+      tra[1] ^= SB;
+    }
   }
-  const float inv = (lrow > 0.f) ? 1.f / lrow : 0.f;
-  if (half == 0) LSE[(int64_t)h * N + row0 + 32 * w + l32] = (lrow > 0.f) ? (mrow + log2f(lrow)) * kLn2 : -INFINITY;
-  uint16_t* sO = sK;
-  // pass 0 writes O rounded to bf16, pass 1 (if requested) its rounding residual
-  for (int pass = 0; pass < (Olo ? 2 : 1); ++pass) {
-    __syncthreads();
+  // merge the key halves: the kh = 1 wave of each row half hands (O, m, l) over through LDS
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smem);                 // [rh][DB * 16][64 lanes]
+  float* xm = reinterpret_cast<float*>(smem + 2 * T);         // [rh][m | l][32 rows]
+  if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[((rh * DB + db) * 16 + r) * 64 + lane] = oacc[db][r];
+    if (half == 0) {
+      xm[rh * 64 + l32] = mrow;
+      xm[rh * 64 + 32 + l32] = lrow;
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = xm[rh * 64 + l32], l1 = xm[rh * 64 + 32 + l32];
+    const float m = fmaxf(mrow, m1);
+    const float a0 = (mrow == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrow - m);
+    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    const float l = lrow * a0 + l1 * a1;
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    if (half == 0) LSE[(int64_t)h * N + myrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
+    // the lane holds O[myrow][d = 32db + 8jj + 4half + e]: O rounded to bf16 and, if requested,
+    // its rounding residual, 8 bytes per lane and store
+    uint16_t* orow = O + hoff + (int64_t)myrow * D + 4 * half;
+    uint16_t* rrow = Olo ? Olo + hoff + (int64_t)myrow * D + 4 * half : nullptr;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float ov[4];
+        float ov[4], rv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ov[e] = oacc[db][4 * jj + e] * inv;
-          if (pass) ov[e] -= bf16_to_f32(f32_to_bf16(ov[e]));
+          const int r = 4 * jj + e;
+          ov[e] = (oacc[db][r] * a0 + xo[((rh * DB + db) * 16 + r) * 64 + lane] * a1) * inv;
+          rv[e] = ov[e] - bf16_to_f32(f32_to_bf16(ov[e]));
         }
         u32x2 pk;
         pk[0] = pack_bf16x2(ov[0], ov[1]);
         pk[1] = pack_bf16x2(ov[2], ov[3]);
-        *reinterpret_cast<u32x2*>(sO + (32 * w + l32) * C::KP + 32 * db + 8 * jj + 4 * half) = pk;
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj) = pk;
+        if (rrow) {
+          pk[0] = pack_bf16x2(rv[0], rv[1]);
+          pk[1] = pack_bf16x2(rv[2], rv[3]);
+          *reinterpret_cast<u32x2*>(rrow + 32 * db + 8 * jj) = pk;
+        }
       }
-    __syncthreads();
-    copy_out<D>((pass ? Olo : O) + hoff + (int64_t)row0 * D, sO, tid);
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // backward, query-major: dQ
 
+// Same decomposition as the forward: wave w owns query rows 32*(w&1).. and keys 32*(w>>1).. of
+// every tile; the two partial dQ of a row half are summed at the end.
 template <int D>
-__global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                               const float* __restrict__ LSE, const float* __restrict__ delta,
+                                               const float* __restrict__ LSE2, const float* __restrict__ delta,
                                                float* __restrict__ dQ, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
                                                float scale2, float sm_scale) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[C::TILE];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  constexpr int T = 64 * D;
+  constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
+  constexpr uint32_t SB = 4 * T;  // bytes of one stage (K tile, V tile)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T];  // two stages
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = w & 1, kh = w >> 1;
   const int h = blockIdx.y;
   const int natoms = N >> 6;
   const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
@@ -372,204 +451,279 @@ __global__ __launch_bounds__(128, 1) void k_dq(const uint16_t* __restrict__ Q, c
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
-  const int myrow = row0 + 32 * w + l32;
+  const int myrow = row0 + 32 * rh + l32;
 
-  bf16x8 qop[C::DS], doop[C::DS];
+  bf16x8 qop[DS], doop[DS];
   {
     const uint16_t* qr = Q + hoff + (int64_t)myrow * D + (D / 2) * half;
     const uint16_t* dr = dO + hoff + (int64_t)myrow * D + (D / 2) * half;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
+    for (int s = 0; s < DS; ++s) {
       qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 8 * s));
       doop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(dr + 8 * s));
     }
   }
-  const float lse2 = LSE[(int64_t)h * N + myrow] * kLog2e;
+  const float lse2 = LSE2[(int64_t)h * N + myrow];
   const float dl = delta[(int64_t)h * N + myrow];
-  f32x16 dqacc[C::DB];
+  f32x16 dqacc[DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) dqacc[db] = zero16();
+  for (int db = 0; db < DB; ++db) dqacc[db] = zero16();
 
   ListTiles it;
   it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
-  u32x4 kreg[C::NIT], vreg[C::NIT];
+  uint32_t doff[Tile<D>::NI], tra[2];
+  dma_offsets<D>(w, lane, doff);
+  tr_addr<D>(lane, tra);
+  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
+  auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
+    uint16_t* s = smem + soff / 2;
+    dma_tile<D>(Kh + (int64_t)it.kt * D, s, w, doff);
+    dma_tile<D>(Vh + (int64_t)it.kt * D, s + T, w, doff);
+  };
+  auto compute = [&]() __attribute__((always_inline)) {
+    const uint16_t* sK = smem;
+    const uint16_t* sV = smem + T;
+    // S^T = K Q^T, dP^T = V dO^T for this wave's 32 keys x 32 rows
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qop[st], sacc);
+      dpacc = mfma(lds_b128(sV, rowa ^ (st << 4)), doop[st], dpacc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -lse2));
+      sacc[r] = pv * (dpacc[r] - dl);
+    }
+    // dQ^T += K^T dS^T, dS as bf16 head + residual
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      bf16x8 ds_hi, ds_lo;
+      pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 kt_op = tile_rows_op<D>(sK, tra, 32 * kh + 16 * tt, 32 * db);
+        dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
+        dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
+      }
+    }
+  };
   if (it.valid()) {
-    gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
-    gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
-  }
-  while (it.valid()) {
-    __syncthreads();
-    lstore<D>(sK, kreg, tid);
-    lstore<D>(sV, vreg, tid);
-    __syncthreads();
-    it.next();
-    if (it.valid()) {
-      gload<D>(Kh + (int64_t)it.kt * D, kreg, tid);
-      gload<D>(Vh + (int64_t)it.kt * D, vreg, tid);
+    uint32_t soff = 0;
+    stage(0);
+    while (true) {
+      dma_wait();
+      __syncthreads();
+      it.next();
+      const bool more = it.valid();
+      if (more) stage(soff ^ SB);
+      compute();
+      if (!more) break;
+      soff ^= SB;
+      rowa ^= SB;
+      tra[0] ^= SB;
+      tra[1] ^= SB;
     }
+  }
+  // sum the key halves: the kh = 1 wave of each row half hands its partial over through LDS
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smem);  // [rh][DB * 16][64 lanes]
+  if (kh == 1) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc = zero16(), dpacc = zero16();
-      const uint16_t* ka = sK + (32 * kb + l32) * C::KP + (D / 2) * half;
-      const uint16_t* va = sV + (32 * kb + l32) * C::KP + (D / 2) * half;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-        sacc = mfma(as_bf16x8(lds16(ka + 8 * s)), qop[s], sacc);
-        dpacc = mfma(as_bf16x8(lds16(va + 8 * s)), doop[s], dpacc);
-      }
+      for (int r = 0; r < 16; ++r) xo[((rh * DB + db) * 16 + r) * 64 + lane] = dqacc[db][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    // fp32 output: lane holds dQ[myrow][32db + 8jj + 4half + e]
+    float* dqr = dQ + hoff + (int64_t)myrow * D + 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -lse2));
-        sacc[r] = pv * (dpacc[r] - dl);
-      }
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        bf16x8 ds_hi, ds_lo;
-        pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
-        const int t = 2 * kb + tt;
+      for (int jj = 0; jj < 4; ++jj) {
+        float v[4];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 kt_op = lds_rows_operand<D>(sK, 16 * t, 32 * db, lane);
-          dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
-          dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * jj + e;
+          v[e] = (dqacc[db][r] + xo[((rh * DB + db) * 16 + r) * 64 + lane]) * sm_scale;
         }
+        *reinterpret_cast<float4*>(dqr + 32 * db + 8 * jj) = make_float4(v[0], v[1], v[2], v[3]);
       }
-    }
   }
-  // fp32 output: lane holds dQ[myrow][32db + 8jj + 4half + e]
-  float* dqr = dQ + hoff + (int64_t)myrow * D + 4 * half;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float4 v4;
-      v4.x = dqacc[db][4 * jj + 0] * sm_scale;
-      v4.y = dqacc[db][4 * jj + 1] * sm_scale;
-      v4.z = dqacc[db][4 * jj + 2] * sm_scale;
-      v4.w = dqacc[db][4 * jj + 3] * sm_scale;
-      *reinterpret_cast<float4*>(dqr + 32 * db + 8 * jj) = v4;
-    }
 }
 
 // ------------------------------------------------------------------------------------------
 // backward, key-major: dK, dV
 
+// Workgroup = 4 waves on one 64-key atom.  Wave w owns keys 32*(w&1).. of the atom and, of every
+// staged 64-row query tile (the tiles of the query blocks whose lists hold this key block), query
+// rows 32*(w>>1)..; the two partial dK, dV of a key half are summed at the end.  A stage holds
+// the Q and dO tiles plus the tile's lse2 and delta rows.
 template <int D>
-__global__ __launch_bounds__(128, 1) void k_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                 const float* __restrict__ LSE, const float* __restrict__ delta,
+                                                 const float* __restrict__ LSE2, const float* __restrict__ delta,
                                                  float* __restrict__ dK, float* __restrict__ dV,
                                                  const int32_t* __restrict__ block_start,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
                                                  int N, float scale2, float sm_scale) {
-  using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[C::TILE];
-  __shared__ __attribute__((aligned(16))) float sL[64];
-  __shared__ __attribute__((aligned(16))) float sD[64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  constexpr int T = 64 * D;
+  constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
+  constexpr uint32_t SB = 4 * T;  // bytes of one stage's tiles (Q, dO)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T + 1024];  // two stages + lse2/delta
+  float* sld = reinterpret_cast<float*>(smem + 4 * T);                      // [stage][256 floats]
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = w & 1, qh = w >> 1;
   const int h = blockIdx.y;
   const int natoms = N >> 6;
   const int key0 = xcd_atom(blockIdx.x, natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int kb_idx = block_of_row(bs, nbmax, key0);
   const int64_t hoff = (int64_t)h * N * D;
-  const int mykey = key0 + 32 * w + l32;
+  const int mykey = key0 + 32 * kh + l32;
 
-  bf16x8 kop[C::DS], vop[C::DS];
+  bf16x8 kop[DS], vop[DS];
   {
     const uint16_t* kr = K + hoff + (int64_t)mykey * D + (D / 2) * half;
     const uint16_t* vr = V + hoff + (int64_t)mykey * D + (D / 2) * half;
 #pragma unroll
-    for (int s = 0; s < C::DS; ++s) {
+    for (int s = 0; s < DS; ++s) {
       kop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 8 * s));
       vop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(vr + 8 * s));
     }
   }
-  f32x16 dkacc[C::DB], dvacc[C::DB];
+  f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
     dkacc[db] = zero16();
     dvacc[db] = zero16();
   }
 
   MaskTiles it;
   it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw);
-  u32x4 qreg[C::NIT], oreg[C::NIT];
-  float lv = 0.f, dv = 0.f;
-  auto prefetch = [&](int rt) {
-    gload<D>(Q + hoff + (int64_t)rt * D, qreg, tid);
-    gload<D>(dO + hoff + (int64_t)rt * D, oreg, tid);
-    if (tid < 64) {
-      lv = LSE[(int64_t)h * N + rt + tid] * kLog2e;
-      dv = delta[(int64_t)h * N + rt + tid];
+  uint32_t doff[Tile<D>::NI], tra[2];
+  dma_offsets<D>(w, lane, doff);
+  tr_addr<D>(lane, tra);
+  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  uint32_t rowa = row_addr<D>(32 * qh + l32) ^ ((CH * half) << 4);
+  // byte address of lse2[32qh + 4half] in the stage's row-statistics block (delta at +256)
+  uint32_t lda = 2 * SB + 4 * (32 * qh + 4 * half);
+  const float* L2h = LSE2 + (int64_t)h * N;
+  const float* Dh = delta + (int64_t)h * N;
+  // lse2 and delta of a tile's 64 rows: one 1 KB direct load by wave 0, lanes 0-15 fetch lse2,
+  // lanes 16-31 delta (lanes 32-63 repeat them), landing at floats [0, 64) and [64, 128)
+  const int ldl = lane & 31;
+  auto stage = [&](uint32_t soff, int stg) __attribute__((always_inline)) {
+    uint16_t* s = smem + soff / 2;
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds((gbl_void*)((ldl < 16 ? L2h : Dh) + it.rt + 4 * (ldl & 15)),
+                                       (lds_void*)(sld + 256 * stg), 16, 0, 0);
+    dma_tile<D>(Q + hoff + (int64_t)it.rt * D, s, w, doff);
+    dma_tile<D>(dO + hoff + (int64_t)it.rt * D, s + T, w, doff);
+  };
+  auto compute = [&]() __attribute__((always_inline)) {
+    const uint16_t* sQ = smem;
+    const uint16_t* sdO = smem + T;
+
+    // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 keys
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      sacc = mfma(lds_b128(sQ, rowa ^ (st << 4)), kop[st], sacc);
+      dpacc = mfma(lds_b128(sdO, rowa ^ (st << 4)), vop[st], dpacc);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const u32x4 L4 = __builtin_bit_cast(u32x4, lds_b128(smem, lda + 32 * jj));
+      const u32x4 D4 = __builtin_bit_cast(u32x4, lds_b128(smem, lda + 256 + 32 * jj));
+      const float Lv[4] = {__uint_as_float(L4[0]), __uint_as_float(L4[1]), __uint_as_float(L4[2]),
+                           __uint_as_float(L4[3])};
+      const float Dv[4] = {__uint_as_float(D4[0]), __uint_as_float(D4[1]), __uint_as_float(D4[2]),
+                           __uint_as_float(D4[3])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * jj + e;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -Lv[e]));
+        sacc[r] = pv;
+        dpacc[r] = pv * (dpacc[r] - Dv[e]);
+      }
+    }
+    // dV += P^T dO, then dK += dS^T Q (P and dS as bf16 head + residual); the phases are kept
+    // apart so that only one split operand set is live at a time
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 pa_hi, pa_lo;
+      pack8_split(sacc, 8 * t, pa_hi, pa_lo);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 dot_op = tile_rows_op<D>(sdO, tra, 32 * qh + 16 * t, 32 * db);
+        dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
+        dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 da_hi, da_lo;
+      pack8_split(dpacc, 8 * t, da_hi, da_lo);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 qt_op = tile_rows_op<D>(sQ, tra, 32 * qh + 16 * t, 32 * db);
+        dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
+        dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
+      }
     }
   };
-  if (it.valid()) prefetch(it.rt);
-  while (it.valid()) {
-    __syncthreads();
-    lstore<D>(sQ, qreg, tid);
-    lstore<D>(sdO, oreg, tid);
-    if (tid < 64) {
-      sL[tid] = lv;
-      sD[tid] = dv;
-    }
-    __syncthreads();
-    it.next();
-    if (it.valid()) prefetch(it.rt);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // S = Q K^T and dP = dO V^T for query rows 32rb.. of the tile, this wave's 32 keys
-      f32x16 sacc = zero16(), dpacc = zero16();
-      const uint16_t* qa = sQ + (32 * rb + l32) * C::KP + (D / 2) * half;
-      const uint16_t* oa = sdO + (32 * rb + l32) * C::KP + (D / 2) * half;
-#pragma unroll
-      for (int s = 0; s < C::DS; ++s) {
-        sacc = mfma(as_bf16x8(lds16(qa + 8 * s)), kop[s], sacc);
-        dpacc = mfma(as_bf16x8(lds16(oa + 8 * s)), vop[s], dpacc);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rr = 32 * rb + 8 * jj + 4 * half;
-        const float4 L4 = *reinterpret_cast<const float4*>(sL + rr);
-        const float4 D4 = *reinterpret_cast<const float4*>(sD + rr);
-        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * jj + e;
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale2, -Lv[e]));
-          sacc[r] = pv;
-          dpacc[r] = pv * (dpacc[r] - Dv[e]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 pa_hi, pa_lo, da_hi, da_lo;
-        pack8_split(sacc, 8 * t, pa_hi, pa_lo);
-        pack8_split(dpacc, 8 * t, da_hi, da_lo);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const bf16x8 dot_op = lds_rows_operand<D>(sdO, 32 * rb + 16 * t, 32 * db, lane);
-          const bf16x8 qt_op = lds_rows_operand<D>(sQ, 32 * rb + 16 * t, 32 * db, lane);
-          dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
-          dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
-          dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
-          dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
-        }
-      }
+  if (it.valid()) {
+    uint32_t soff = 0;
+    int stg = 0;
+    stage(0, 0);
+    while (true) {
+      dma_wait();
+      __syncthreads();
+      it.next();
+      const bool more = it.valid();
+      if (more) stage(soff ^ SB, stg ^ 1);
+      compute();
+      if (!more) break;
+      soff ^= SB;
+      stg ^= 1;
+      rowa ^= SB;
+      tra[0] ^= SB;
+      tra[1] ^= SB;
+      lda ^= 1024;
     }
   }
-  // fp32 outputs: accumulators hold [key = 8jj + 4half + e][d = 32db + l32]; 32 lanes store
-  // 128 contiguous bytes of one key row per instruction
+  // sum the query halves: the qh = 1 wave of each key half hands its partials over through LDS
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(smem);  // [kh][dK | dV][DB * 16][64 lanes]
+  if (qh == 1) {
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 32 * w + 8 * (r >> 2) + 4 * half + (r & 3);
-      const int64_t off = hoff + (int64_t)key * D + 32 * db + l32;
-      dK[off] = dkacc[db][r] * sm_scale;
-      dV[off] = dvacc[db][r];
-    }
+      for (int r = 0; r < 16; ++r) {
+        xo[(((2 * kh + 0) * DB + db) * 16 + r) * 64 + lane] = dkacc[db][r];
+        xo[(((2 * kh + 1) * DB + db) * 16 + r) * 64 + lane] = dvacc[db][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    // fp32 outputs: accumulators hold [key = 8jj + 4half + e][d = 32db + l32]; 32 lanes store
+    // 128 contiguous bytes of one key row per instruction
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int64_t off = hoff + (int64_t)key * D + 32 * db + l32;
+        dK[off] = (dkacc[db][r] + xo[(((2 * kh + 0) * DB + db) * 16 + r) * 64 + lane]) * sm_scale;
+        dV[off] = dvacc[db][r] + xo[(((2 * kh + 1) * DB + db) * 16 + r) * 64 + lane];
+      }
+  }
 }
 
 }  // namespace
@@ -581,18 +735,18 @@ prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cn
   const float scale2 = sm_scale * kLog2e;
   KernelTrace tr("k_fwd", st);
   if (g.d == 64)
-    hipLaunchKernelGGL(k_fwd<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+    hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
                        (int)g.N, scale2);
   else
-    hipLaunchKernelGGL(k_fwd<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+    hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
                        (int)g.N, scale2);
   return check_launch("k_fwd");
 }
 
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
-                             const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                             const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                              const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
                              hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
@@ -600,24 +754,24 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
   {
     KernelTrace tr("k_dq", st);
     if (g.d == 64)
-      hipLaunchKernelGGL(k_dq<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                         (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
+      hipLaunchKernelGGL(k_dq<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
                          (int)g.N, scale2, sm_scale);
     else
-      hipLaunchKernelGGL(k_dq<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                         (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
+      hipLaunchKernelGGL(k_dq<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
                          (int)g.N, scale2, sm_scale);
   }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
   KernelTrace tr("k_dkdv", st);
   if (g.d == 64)
-    hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw,
+    hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
                        g.hpg, (int)g.N, scale2, sm_scale);
   else
-    hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw,
+    hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
                        g.hpg, (int)g.N, scale2, sm_scale);
   return check_launch("k_dkdv");
 }
