@@ -41,7 +41,7 @@ int g_trace_n = 0;
 KernelTrace::KernelTrace(const char* kernel, hipStream_t st) : st_(st) {
   for (int i = 0; i < g_trace_n; ++i)
     if (strcmp(g_trace[i].name, kernel) == 0) {
-      hipEventRecord(g_trace[i].start, st);
+      (void)hipEventRecord(g_trace[i].start, st);
       stop_ = g_trace[i].stop;
       return;
     }
