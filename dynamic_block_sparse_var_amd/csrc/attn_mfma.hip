@@ -2,12 +2,15 @@
 // (RG M3: online-softmax attention solely across the selected key blocks S_i).
 //
 // Work decomposition.  Every block holds 64, 128 or 256 rows and starts on a multiple of 64,
-// so the unit of work is a 64-row "atom" of one head.  A workgroup is two wave64s; each wave
-// owns 32 rows (or 32 keys) of the atom.  The other operand is streamed in 64-row tiles that
-// are staged once per workgroup in LDS, row-major, and shared by both waves; the next tile's
-// global loads are issued before the current tile is computed (register double buffering).
-// Atoms are assigned so that each of the 8 XCDs walks a contiguous range of atoms
-// (neighbouring blocks tend to select the same key blocks, which then stay in that XCD's L2).
+// so the unit of work is a 64-row "atom" of one head, one workgroup of four wave64s per atom.
+// The other operand is streamed in 64-row tiles (the selected key blocks of a query atom, or
+// the query blocks that selected a key atom), double-buffered in LDS: the direct global->LDS
+// loads of tile i+1 are in flight while tile i is computed, one barrier per tile.  Within a
+// tile, wave w takes 32 of the atom's rows (forward, dQ: query rows 32*(w&1)..; dK/dV: keys
+// 32*(w&1)..) against 32 of the tile's rows (32*(w>>1)..), and the two waves that share the
+// atom rows combine their partial results once at the end.  Atoms are assigned so that each
+// of the 8 XCDs walks a contiguous range of atoms (neighbouring blocks tend to select the same
+// key blocks, which may then still be in that XCD's L2).
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16): operand A holds A[m = lane%32][8 k-values],
 // operand B holds B[8 k-values][n = lane%32]; both use lane/32 to pick which half of the 16
@@ -23,8 +26,8 @@
 //    receives element i%4 of the 8-byte reads of lanes 4e + i/4, e = 0..3).
 //
 // Forward:  S^T = K Q^T (A = K tile, B = Q rows in registers), online softmax per query row
-//           (each lane owns one row; the other 32 keys of a tile sit in lane ^ 32; the
-//           running max is only raised when a tile exceeds it by 2^8, so the O rescale is
+//           (a lane owns one row for 16 of the wave's 32 keys, lane ^ 32 the other 16; the
+//           running max is only raised when a tile exceeds it by 2^16, so the O rescale is
 //           rare), O^T += V^T P^T with P split into a bf16 head and residual.
 // dQ:       S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - delta), dQ^T += K^T dS^T.
 // dK, dV:   key-major: for every query block whose list contains the key block (transposed
@@ -32,6 +35,8 @@
 // Products with P and dS use a bf16 head plus a bf16 residual of the fp32 value, so the
 // results keep fp32-level accuracy.
 #include <math.h>
+
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -49,7 +54,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
+// log2 units the running max may lag behind: probabilities stay below 2^16 and row sums below
+// 2^16 times the key count, far inside fp32 range
+constexpr float kRescaleSlack = 16.f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -173,57 +180,120 @@ __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* s, uint32_t byte) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s) + byte));
 }
 
-__device__ __forceinline__ u32x2 lds_tr_at(const uint16_t* s, uint32_t byte) {
-  return __builtin_bit_cast(
-      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(reinterpret_cast<const char*>(s) + byte)));
+
+// Operands holding X[R0 + 8*(e/4) + 4*(lane/32) + e%4][32*db + lane%32], e = 0..7, of a
+// swizzled tile X, for consecutive db starting at DB0 -- the lane's 8 k-slots when the product
+// reduces over rows.  a[b] are the lane's absolute LDS addresses for the tile at smem byte 0,
+// rows R0 = Rw and db = 0 (tr_table); column block db is reached by XOR-ing 64*db into the
+// address, and OFF (an immediate) adds the tile's byte offset and 2*D*(R0 - Rw).  The reads are
+// issued in one asm block that also waits for them: the compiler treats a transposing read as
+// possibly aliasing the direct loads in flight into the other stage and would otherwise wait
+// for those loads first.  Ordering against this stage's loads is given by dma_wait() and the
+// barrier that precede every compute step.
+template <int D>
+__device__ __forceinline__ void tr_table(const uint16_t* smem, int lane, int Rw, uint32_t (&a)[2]) {
+  uint32_t tr[2];
+  tr_addr<D>(lane, tr);
+  const uint32_t sbase = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)smem);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) a[b] = sbase + tr[b] + 2 * D * Rw;
 }
 
-// Operand holding X[R0 + 8*(e/4) + 4*(lane/32) + e%4][D0 + lane%32], e = 0..7, of a swizzled
-// tile X -- the lane's 8 k-slots when the product reduces over rows.
-template <int D>
-__device__ __forceinline__ bf16x8 tile_rows_op(const uint16_t* s, const uint32_t (&tr)[2], int R0, int D0) {
-  const u32x2 a = lds_tr_at(s, (tr[0] ^ (2 * D0)) + 2 * D * R0);
-  const u32x2 b = lds_tr_at(s, (tr[1] ^ (2 * D0)) + 2 * D * R0);
+__device__ __forceinline__ bf16x8 join_tr(u32x2 lo, u32x2 hi) {
   u32x4 v;
-  v[0] = a[0];
-  v[1] = a[1];
-  v[2] = b[0];
-  v[3] = b[1];
+  v[0] = lo[0];
+  v[1] = lo[1];
+  v[2] = hi[0];
+  v[3] = hi[1];
   return as_bf16x8(v);
 }
+
+template <int OFF, int DB0>
+__device__ __forceinline__ void tr_ops(const uint32_t (&a)[2], bf16x8 (&op)[4]) {
+  u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0] ^ (64 * DB0)), "v"(a[1] ^ (64 * DB0)), "v"(a[0] ^ (64 * DB0 + 64)), "v"(a[1] ^ (64 * DB0 + 64)),
+        "v"(a[0] ^ (64 * DB0 + 128)), "v"(a[1] ^ (64 * DB0 + 128)), "v"(a[0] ^ (64 * DB0 + 192)),
+        "v"(a[1] ^ (64 * DB0 + 192)), "i"(OFF));
+  op[0] = join_tr(r0, r1);
+  op[1] = join_tr(r2, r3);
+  op[2] = join_tr(r4, r5);
+  op[3] = join_tr(r6, r7);
+}
+
+template <int OFF, int DB0>
+__device__ __forceinline__ void tr_ops(const uint32_t (&a)[2], bf16x8 (&op)[2]) {
+  u32x2 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0] ^ (64 * DB0)), "v"(a[1] ^ (64 * DB0)), "v"(a[0] ^ (64 * DB0 + 64)), "v"(a[1] ^ (64 * DB0 + 64)),
+        "i"(OFF));
+  op[0] = join_tr(r0, r1);
+  op[1] = join_tr(r2, r3);
+}
+
+// The tile walkers below fetch the bounds of up to 64 upcoming blocks at a time, one block per
+// lane (vector loads), and take the current block's bounds from its lane with v_readlane, so
+// walking a list costs no dependent memory round trip per block.
 
 // Walks the 64-row tiles of the key blocks in a selection list (wave-uniform state).
 struct ListTiles {
   const int32_t* list;
   const int32_t* bs;
-  int cnt, sidx, kt, kend;
-  __device__ void begin(const int32_t* l, const int32_t* b, int c) {
+  int cnt, base, k, kt, kend;
+  int s_l, e_l;  // per lane: bounds of block list[base + lane]
+  __device__ void fetch(int lane) {
+    const int i = base + lane;
+    const int j = (i < cnt) ? list[i] : 0;
+    s_l = bs[j];
+    e_l = bs[j + 1];
+  }
+  __device__ void take() {
+    kt = __builtin_amdgcn_readlane(s_l, k);
+    kend = __builtin_amdgcn_readlane(e_l, k);
+  }
+  __device__ void begin(const int32_t* l, const int32_t* b, int c, int lane) {
     list = l;
     bs = b;
     cnt = c;
-    sidx = 0;
+    base = k = 0;
     kt = kend = 0;
     if (cnt > 0) {
-      const int j = list[0];
-      kt = bs[j];
-      kend = bs[j + 1];
+      fetch(lane);
+      take();
     }
   }
-  __device__ bool valid() const { return sidx < cnt; }
-  __device__ void next() {
+  __device__ bool valid() const { return base + k < cnt; }
+  __device__ void next(int lane) {
     kt += 64;
     if (kt >= kend) {
-      ++sidx;
-      if (sidx < cnt) {
-        const int j = list[sidx];
-        kt = bs[j];
-        kend = bs[j + 1];
+      if (++k == 64) {
+        base += 64;
+        k = 0;
+        if (base < cnt) fetch(lane);
       }
+      if (base + k < cnt) take();
     }
   }
 };
 
-// Walks the 64-row tiles of the query blocks whose bit is set in a transposed-selection row.
+// Walks the 64-row tiles of the query blocks whose bit is set in a transposed-selection row
+// (wave-uniform state, scalar loads).
 struct MaskTiles {
   const uint32_t* mrow;
   const int32_t* bs;
@@ -252,7 +322,7 @@ struct MaskTiles {
     if (nw > 0) advance_block();
   }
   __device__ bool valid() const { return wi < nw; }
-  __device__ void next() {
+  __device__ void next(int) {
     rt += 64;
     if (rt >= rend) advance_block();
   }
@@ -302,11 +372,11 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   float mrow = -INFINITY, lrow = 0.f;
 
   ListTiles it;
-  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
-  uint32_t doff[Tile<D>::NI], tra[2];
+  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb], lane);
+  uint32_t doff[Tile<D>::NI], tav[2];
   dma_offsets<D>(w, lane, doff);
-  tr_addr<D>(lane, tra);
-  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  tr_table<D>(smem, lane, 32 * kh, tav);
+  // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
   auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
     uint16_t* s = smem + soff / 2;
@@ -315,19 +385,20 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   };
   auto compute = [&]() __attribute__((always_inline)) {
     const uint16_t* sK = smem;
-    const uint16_t* sV = smem + T;
     // S^T = K Q^T for this wave's 32 keys x 32 rows
     f32x16 sacc = zero16();
 #pragma unroll
     for (int st = 0; st < DS; ++st) sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qop[st], sacc);
-    // online softmax in base 2 (logits scaled by sm_scale * log2 e); the running max is raised
-    // (and O rescaled) only when this tile exceeds it by more than the slack
+    // online softmax in base 2 (logits scaled by sm_scale * log2 e).  The running max, shared by
+    // the two lanes of a row (lane and lane ^ 32 hold 16 of the tile's 32 keys each), is raised
+    // and O rescaled only when a tile exceeds it by more than the slack, so the cross-lane max
+    // is formed only then; each lane keeps its own partial row sum, added up after the loop.
     float mx = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale2;
+    mx *= scale2;
     if (__any(mx > mrow + kRescaleSlack)) {
-      const float mnew = fmaxf(mrow, mx);
+      const float mnew = fmaxf(mrow, fmaxf(mx, __shfl_xor(mx, 32, 64)));
       const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
       lrow *= alpha;
 #pragma unroll
@@ -341,19 +412,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
       sacc[r] = pv;
       psum += pv;
     }
-    lrow += psum + __shfl_xor(psum, 32, 64);
+    lrow += psum;
     // O^T += V^T P^T, P as bf16 head + residual
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      bf16x8 p_hi, p_lo;
+    auto pv = [&](auto ttc) __attribute__((always_inline)) {
+      constexpr int tt = decltype(ttc)::value;
+      bf16x8 p_hi, p_lo, vt[DB];
       pack8_split(sacc, 8 * tt, p_hi, p_lo);
+      tr_ops<2 * T + 32 * D * tt, 0>(tav, vt);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 vt_op = tile_rows_op<D>(sV, tra, 32 * kh + 16 * tt, 32 * db);
-        oacc[db] = mfma(vt_op, p_hi, oacc[db]);
-        oacc[db] = mfma(vt_op, p_lo, oacc[db]);
+        oacc[db] = mfma(vt[db], p_hi, oacc[db]);
+        oacc[db] = mfma(vt[db], p_lo, oacc[db]);
       }
-    }
+    };
+    pv(std::integral_constant<int, 0>{});
+    pv(std::integral_constant<int, 1>{});
   };
   if (it.valid()) {
     uint32_t soff = 0;
@@ -361,17 +434,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
     while (true) {
       dma_wait();
       __syncthreads();
-      it.next();
+      it.next(lane);
       const bool more = it.valid();
       if (more) stage(soff ^ SB);
       compute();
       if (!more) break;
       soff ^= SB;
       rowa ^= SB;
-      tra[0] ^= SB;
-      tra[1] ^= SB;
+      const uint32_t step = soff ? SB : (uint32_t)(-(int32_t)SB);
+      tav[0] += step;
+      tav[1] += step;
     }
   }
+  lrow += __shfl_xor(lrow, 32, 64);
   // merge the key halves: the kh = 1 wave of each row half hands (O, m, l) over through LDS
   __syncthreads();
   float* xo = reinterpret_cast<float*>(smem);                 // [rh][DB * 16][64 lanes]
@@ -470,11 +545,11 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
   for (int db = 0; db < DB; ++db) dqacc[db] = zero16();
 
   ListTiles it;
-  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb]);
-  uint32_t doff[Tile<D>::NI], tra[2];
+  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb], lane);
+  uint32_t doff[Tile<D>::NI], tak[2];
   dma_offsets<D>(w, lane, doff);
-  tr_addr<D>(lane, tra);
-  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  tr_table<D>(smem, lane, 32 * kh, tak);
+  // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
   auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
     uint16_t* s = smem + soff / 2;
@@ -497,17 +572,19 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
       sacc[r] = pv * (dpacc[r] - dl);
     }
     // dQ^T += K^T dS^T, dS as bf16 head + residual
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      bf16x8 ds_hi, ds_lo;
+    auto dsk = [&](auto ttc) __attribute__((always_inline)) {
+      constexpr int tt = decltype(ttc)::value;
+      bf16x8 ds_hi, ds_lo, kt[DB];
       pack8_split(sacc, 8 * tt, ds_hi, ds_lo);
+      tr_ops<32 * D * tt, 0>(tak, kt);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 kt_op = tile_rows_op<D>(sK, tra, 32 * kh + 16 * tt, 32 * db);
-        dqacc[db] = mfma(kt_op, ds_hi, dqacc[db]);
-        dqacc[db] = mfma(kt_op, ds_lo, dqacc[db]);
+        dqacc[db] = mfma(kt[db], ds_hi, dqacc[db]);
+        dqacc[db] = mfma(kt[db], ds_lo, dqacc[db]);
       }
-    }
+    };
+    dsk(std::integral_constant<int, 0>{});
+    dsk(std::integral_constant<int, 1>{});
   };
   if (it.valid()) {
     uint32_t soff = 0;
@@ -515,15 +592,16 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
     while (true) {
       dma_wait();
       __syncthreads();
-      it.next();
+      it.next(lane);
       const bool more = it.valid();
       if (more) stage(soff ^ SB);
       compute();
       if (!more) break;
       soff ^= SB;
       rowa ^= SB;
-      tra[0] ^= SB;
-      tra[1] ^= SB;
+      const uint32_t step = soff ? SB : (uint32_t)(-(int32_t)SB);
+      tak[0] += step;
+      tak[1] += step;
     }
   }
   // sum the key halves: the kh = 1 wave of each row half hands its partial over through LDS
@@ -572,8 +650,9 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
   constexpr uint32_t SB = 4 * T;  // bytes of one stage's tiles (Q, dO)
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T + 1024];  // two stages + lse2/delta
-  float* sld = reinterpret_cast<float*>(smem + 4 * T);                      // [stage][256 floats]
+  // two stages of (Q, dO) tiles, then [stage][lse2 | delta][256] floats
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T + 2048];
+  float* sld = reinterpret_cast<float*>(smem + 4 * T);
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = w & 1, qh = w >> 1;
@@ -604,23 +683,23 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 
   MaskTiles it;
   it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw);
-  uint32_t doff[Tile<D>::NI], tra[2];
+  uint32_t doff[Tile<D>::NI], taq[2];
   dma_offsets<D>(w, lane, doff);
-  tr_addr<D>(lane, tra);
-  // per-lane read addresses of the stage being computed (the stage bit is toggled per tile)
+  tr_table<D>(smem, lane, 32 * qh, taq);
+  // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * qh + l32) ^ ((CH * half) << 4);
   // byte address of lse2[32qh + 4half] in the stage's row-statistics block (delta at +256)
-  uint32_t lda = 2 * SB + 4 * (32 * qh + 4 * half);
+  uint32_t lda = 2 * SB + 4 * (32 * qh + 4 * half);  // lse2 rows; delta at +1024 bytes
   const float* L2h = LSE2 + (int64_t)h * N;
   const float* Dh = delta + (int64_t)h * N;
-  // lse2 and delta of a tile's 64 rows: one 1 KB direct load by wave 0, lanes 0-15 fetch lse2,
-  // lanes 16-31 delta (lanes 32-63 repeat them), landing at floats [0, 64) and [64, 128)
-  const int ldl = lane & 31;
+  // lse2 (wave 0) and delta (wave 1) of a tile's 64 rows: one 1 KB direct load each, lanes
+  // 0-15 fetching the 256 bytes (the other lanes repeat them)
+  const float* ldsrc = (w == 0) ? L2h : Dh;
   auto stage = [&](uint32_t soff, int stg) __attribute__((always_inline)) {
     uint16_t* s = smem + soff / 2;
-    if (w == 0)
-      __builtin_amdgcn_global_load_lds((gbl_void*)((ldl < 16 ? L2h : Dh) + it.rt + 4 * (ldl & 15)),
-                                       (lds_void*)(sld + 256 * stg), 16, 0, 0);
+    if (w < 2)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(ldsrc + it.rt + 4 * (lane & 15)),
+                                       (lds_void*)(sld + 512 * stg + 256 * w), 16, 0, 0);
     dma_tile<D>(Q + hoff + (int64_t)it.rt * D, s, w, doff);
     dma_tile<D>(dO + hoff + (int64_t)it.rt * D, s + T, w, doff);
   };
@@ -638,7 +717,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const u32x4 L4 = __builtin_bit_cast(u32x4, lds_b128(smem, lda + 32 * jj));
-      const u32x4 D4 = __builtin_bit_cast(u32x4, lds_b128(smem, lda + 256 + 32 * jj));
+      const u32x4 D4 = __builtin_bit_cast(u32x4, lds_b128(smem, lda + 1024 + 32 * jj));
       const float Lv[4] = {__uint_as_float(L4[0]), __uint_as_float(L4[1]), __uint_as_float(L4[2]),
                            __uint_as_float(L4[3])};
       const float Dv[4] = {__uint_as_float(D4[0]), __uint_as_float(D4[1]), __uint_as_float(D4[2]),
@@ -654,29 +733,43 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
     // dV += P^T dO, then dK += dS^T Q (P and dS as bf16 head + residual); the phases are kept
     // apart so that only one split operand set is live at a time
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 pa_hi, pa_lo;
+    auto pdo = [&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      bf16x8 pa_hi, pa_lo, dot[2];
       pack8_split(sacc, 8 * t, pa_hi, pa_lo);
+      auto half_db = [&](auto dpc) __attribute__((always_inline)) {
+        constexpr int dp = decltype(dpc)::value;
+        tr_ops<2 * T + 32 * D * t, 2 * dp>(taq, dot);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 dot_op = tile_rows_op<D>(sdO, tra, 32 * qh + 16 * t, 32 * db);
-        dvacc[db] = mfma(pa_hi, dot_op, dvacc[db]);
-        dvacc[db] = mfma(pa_lo, dot_op, dvacc[db]);
-      }
-    }
+        for (int j = 0; j < 2; ++j) {
+          dvacc[2 * dp + j] = mfma(pa_hi, dot[j], dvacc[2 * dp + j]);
+          dvacc[2 * dp + j] = mfma(pa_lo, dot[j], dvacc[2 * dp + j]);
+        }
+      };
+      half_db(std::integral_constant<int, 0>{});
+      if constexpr (DB == 4) half_db(std::integral_constant<int, 1>{});
+    };
+    pdo(std::integral_constant<int, 0>{});
+    pdo(std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bf16x8 da_hi, da_lo;
+    auto dsq = [&](auto tc) __attribute__((always_inline)) {
+      constexpr int t = decltype(tc)::value;
+      bf16x8 da_hi, da_lo, qt[2];
       pack8_split(dpacc, 8 * t, da_hi, da_lo);
+      auto half_db = [&](auto dpc) __attribute__((always_inline)) {
+        constexpr int dp = decltype(dpc)::value;
+        tr_ops<32 * D * t, 2 * dp>(taq, qt);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 qt_op = tile_rows_op<D>(sQ, tra, 32 * qh + 16 * t, 32 * db);
-        dkacc[db] = mfma(da_hi, qt_op, dkacc[db]);
-        dkacc[db] = mfma(da_lo, qt_op, dkacc[db]);
-      }
-    }
+        for (int j = 0; j < 2; ++j) {
+          dkacc[2 * dp + j] = mfma(da_hi, qt[j], dkacc[2 * dp + j]);
+          dkacc[2 * dp + j] = mfma(da_lo, qt[j], dkacc[2 * dp + j]);
+        }
+      };
+      half_db(std::integral_constant<int, 0>{});
+      if constexpr (DB == 4) half_db(std::integral_constant<int, 1>{});
+    };
+    dsq(std::integral_constant<int, 0>{});
+    dsq(std::integral_constant<int, 1>{});
   };
   if (it.valid()) {
     uint32_t soff = 0;
@@ -685,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
     while (true) {
       dma_wait();
       __syncthreads();
-      it.next();
+      it.next(lane);
       const bool more = it.valid();
       if (more) stage(soff ^ SB, stg ^ 1);
       compute();
@@ -693,9 +786,10 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
       soff ^= SB;
       stg ^= 1;
       rowa ^= SB;
-      tra[0] ^= SB;
-      tra[1] ^= SB;
-      lda ^= 1024;
+      const uint32_t step = soff ? SB : (uint32_t)(-(int32_t)SB);
+      taq[0] += step;
+      taq[1] += step;
+      lda ^= 2048;
     }
   }
   // sum the query halves: the qh = 1 wave of each key half hands its partials over through LDS
