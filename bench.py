@@ -314,17 +314,51 @@ def main():
         "k_zone_stats": N * H_ * d * ebytes + 4 * N,
         "k_pool": 2 * N * H_ * d * ebytes + 2 * H_ * pb.nbmax * d * 4,
     }
-    dom = max(MFMA_KERNELS, key=lambda kn: kern_ms[kn])
-    achieved = kflops[dom] / (kern_ms[dom] * 1e-3) / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    # Memory side of the attention kernels: the selected-tile stream this dataflow gathers.  For
+    # every (64-row atom, 64-row tile of a block the atom attends to) unit it reads the two bf16
+    # tiles of the other side (K and V; for dK/dV: Q and dO plus their lse2/delta rows), and
+    # each atom's own rows are read or written once.  A kernel's roofline bound is the side its
+    # arithmetic intensity (algorithmic FLOPs per tile-stream byte) falls on, against the ridge
+    # point peak FLOP/s / peak byte/s.
+    units = pairs // 4096
+    atoms = H_ * (N // 64)
+    tile = 2 * 64 * d * ebytes
+    kalg = {
+        "k_fwd": units * tile + atoms * (3 * 64 * d * ebytes + 64 * 4),
+        "k_dq": units * tile + atoms * (2 * 64 * d * ebytes + 64 * d * 4 + 2 * 64 * 4),
+        "k_dkdv": units * (tile + 2 * 64 * 4) + atoms * (2 * 64 * d * ebytes + 2 * 64 * d * 4),
+    }
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = {}
     tr_path = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tr_path):
         with open(tr_path) as f:
             tr = json.load(f)
-        ent = tr.get(dom)
-        if isinstance(ent, dict) and ent and ent.get("source_sha") == kernel_source_sha() and ent.get("config") == cfg.name:
-            roof["traffic"] = ent["bytes_per_launch"]
+        sha = kernel_source_sha()
+        for kn, ent in tr.items():
+            if isinstance(ent, dict) and ent.get("source_sha") == sha and ent.get("config") == cfg.name:
+                traffic[kn] = ent["bytes_per_launch"]
+    attn_k = {}
+    for kn in MFMA_KERNELS:
+        sec = kern_ms[kn] * 1e-3
+        ai = kflops[kn] / kalg[kn]
+        attn_k[kn] = {"ms": round(kern_ms[kn], 3),
+                      "TFLOP/s": round(kflops[kn] / sec / 1e12, 1),
+                      "mfma_frac": round(kflops[kn] / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "tile_stream_GB": round(kalg[kn] / 1e9, 2),
+                      "GB/s": round(kalg[kn] / sec / 1e9, 1),
+                      "hbm_frac": round(kalg[kn] / sec / 1e9 / PEAK_HBM_GBS, 4),
+                      "flop_per_byte": round(ai, 1),
+                      "bound": "hbm" if ai < ridge else "mfma",
+                      "measured_traffic_GB": round(traffic[kn] / 1e9, 2) if kn in traffic else None}
+    dom = max(MFMA_KERNELS, key=lambda kn: kern_ms[kn])
+    ak = attn_k[dom]
+    if ak["bound"] == "hbm":
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ak["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ak["hbm_frac"], "traffic": traffic.get(dom)}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ak["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ak["mfma_frac"], "traffic": traffic.get(dom)}
     # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
     kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
     kern_ms["k_permute"] = stage_ms["permute_qkv"]
@@ -353,6 +387,7 @@ def main():
         "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
         "kernel_ms": {kn: round(kern_ms[kn], 4) for kn in MFMA_KERNELS},
+        "attn_kernels": attn_k,
         "hbm_stages": hbm,
         "selection": {"executed_pairs": pairs, "mean_key_fraction": round(key_frac, 4), "n_blocks": nblocks,
                       "zones_by_volume": {str(kk): vv for kk, vv in hist.items()}},
