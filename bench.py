@@ -195,11 +195,18 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
+    ap.add_argument("--dense", action="store_true",
+                    help="dense baseline: every key block selected (k = N_b) on the same kernels")
+    ap.add_argument("--fixed-shape", action="store_true",
+                    help="fixed-block ablation: 4x4x4 blocks in every zone, zone statistics and shape "
+                         "assignment skipped")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="no GPU work: read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR/FETCH_SIZE and "
                          "DIR/WRITE_SIZE (taken with --copy-probe-mb on this source tree) and write "
                          "profiles/traffic.json")
     args = ap.parse_args()
+    if args.dense and args.fixed_shape:
+        ap.error("--dense and --fixed-shape are separate variants")
     if args.traffic_from:
         write_traffic(args.traffic_from, args.copy_probe_mb or 4096, args.config)
         return
@@ -231,20 +238,29 @@ def main():
     stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
               "permute_do", "bsa_bwd", "unpermute_grads"]
 
+    fixed = P.fixed_shape_index((4, 4, 4)) if args.fixed_shape else None
+    # dense baseline: every key block selected (k = N_b), the same kernels otherwise
+    k_abs, k_frac = (pb.nbmax, 0.0) if args.dense else (cfg.k_abs, cfg.k_frac)
+
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        P.prism_zone_stats(pb, v, a, cfg.eps, L.g, L.rho, L.zone_audio)
-        mark(1)
-        P.prism_assign_shapes(pb, L.g, L.rho, cfg.tau128, cfg.tau256, L.shape_idx, L.zone_block_off, L.block_start)
+        if fixed is None:
+            P.prism_zone_stats(pb, v, a, cfg.eps, L.g, L.rho, L.zone_audio)
+            mark(1)
+            P.prism_assign_shapes(pb, L.g, L.rho, cfg.tau128, cfg.tau256, L.shape_idx, L.zone_block_off,
+                                  L.block_start)
+        else:  # fixed-block ablation: a1 and a2 replaced by one shape for every zone
+            mark(1)
+            P.prism_fixed_shapes(pb, fixed, L.shape_idx, L.zone_block_off, L.block_start)
         mark(2)
         P.prism_permute(pb, L.shape_idx, 0, [q, k, v], [L.qp, L.kp, L.vp])
         mark(3)
         P.prism_pool_blocks(pb, L.block_start, [L.qp, L.kp], [L.qbar, L.kbar])
         mark(4)
-        P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, cfg.k_abs, cfg.k_frac, cfg.p, L.sel_count,
+        P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, k_abs, k_frac, cfg.p, L.sel_count,
                               L.sel_idx)
         mark(5)
         P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse)
@@ -336,7 +352,8 @@ def main():
             tr = json.load(f)
         sha = kernel_source_sha()
         for kn, ent in tr.items():
-            if isinstance(ent, dict) and ent.get("source_sha") == sha and ent.get("config") == cfg.name:
+            if (isinstance(ent, dict) and ent.get("source_sha") == sha and ent.get("config") == cfg.name
+                    and not (args.dense or args.fixed_shape)):
                 traffic[kn] = ent["bytes_per_launch"]
     attn_k = {}
     for kn in MFMA_KERNELS:
@@ -380,7 +397,10 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded generator; 2K-shaped token grid)",
         "config": {"workload": f"{cfg.name}: {cfg.T}x{cfg.H}x{cfg.W} tokens, {cfg.heads} heads, d {cfg.d}, "
-                               f"k {cfg.k_frac:.0%} p {cfg.p}, forward + backward",
+                               + ("dense (every key block), " if args.dense else
+                                  f"k {cfg.k_frac:.0%} p {cfg.p}, ")
+                               + ("fixed 4x4x4 blocks, " if args.fixed_shape else "")
+                               + "forward + backward",
                    "parallelism": "none (1 GPU)"},
         "attn_fwd_bwd_ms": round(attn_ms, 3),
         "attn_tflops": round(attn_tflops, 1),
@@ -395,7 +415,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (args.dense or args.fixed_shape):
         log("bench: CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(inp, budget_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -82,6 +82,7 @@ def lib():
         "prism_shape_table": (_i32, [_vp]),
         "prism_zone_stats": (_i32, [_PB, _vp, _vp, _f32, _vp, _vp, _vp, _vp]),
         "prism_assign_shapes": (_i32, [_PB, _vp, _vp, _f32, _f32, _vp, _vp, _vp, _vp]),
+        "prism_fixed_shapes": (_i32, [_PB, _i32, _vp, _vp, _vp, _vp]),
         "prism_permute": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp, _vp]),
         "prism_pool_blocks": (_i32, [_PB, _vp, _i32, _vp, _vp, _vp]),
         "prism_select_blocks": (_i32, [_PB, _vp, _vp, _vp, _f32, _i32, _f64, _f64, _vp, _vp, _vp]),
@@ -145,6 +146,16 @@ def prism_zone_stats(pb, v, a, eps, g, rho, zone_audio, stream=None):
 def prism_assign_shapes(pb, g, rho, tau128, tau256, shape_idx, zone_block_off, block_start, stream=None):
     _check(lib().prism_assign_shapes(ctypes.byref(pb), _p(g), _p(rho), tau128, tau256, _p(shape_idx),
                                      _p(zone_block_off), _p(block_start), _stream(stream)), "prism_assign_shapes")
+
+
+def prism_fixed_shapes(pb, shape_index, shape_idx, zone_block_off, block_start, stream=None):
+    _check(lib().prism_fixed_shapes(ctypes.byref(pb), int(shape_index), _p(shape_idx), _p(zone_block_off),
+                                    _p(block_start), _stream(stream)), "prism_fixed_shapes")
+
+
+def fixed_shape_index(edges=(4, 4, 4)) -> int:
+    """Index of a candidate shape (bT, bH, bW) in prism_shape_table (4x4x4 -> 3)."""
+    return prism_shape_table().index(tuple(edges))
 
 
 def prism_permute(pb, shape_idx, inverse, src, dst, stream=None):
@@ -239,8 +250,13 @@ class PrismLayer:
             self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, **e)
 
     # a1..a5
-    def plan(self, v, a, eps=1e-6, tau128=0.5, tau256=0.25, stream=None):
+    def plan(self, v, a, eps=1e-6, tau128=0.5, tau256=0.25, stream=None, fixed_shape=None):
+        """a1 + a2; with fixed_shape (a candidate index) both are replaced by one shape for
+        every zone (the pages' fixed-block ablation)."""
         pb = self.pb
+        if fixed_shape is not None:
+            prism_fixed_shapes(pb, fixed_shape, self.shape_idx, self.zone_block_off, self.block_start, stream)
+            return
         prism_zone_stats(pb, v, a, eps, self.g, self.rho, self.zone_audio if a is not None else None, stream)
         prism_assign_shapes(pb, self.g, self.rho, tau128, tau256, self.shape_idx, self.zone_block_off,
                             self.block_start, stream)
@@ -260,8 +276,9 @@ class PrismLayer:
         prism_permute(pb, self.shape_idx, 1, [self.op], [self.o], stream)
         return self.o
 
-    def forward(self, q, k, v, a, sm_scale, k_abs, k_frac, p, eps=1e-6, tau128=0.5, tau256=0.25, stream=None):
-        self.plan(v, a, eps, tau128, tau256, stream)
+    def forward(self, q, k, v, a, sm_scale, k_abs, k_frac, p, eps=1e-6, tau128=0.5, tau256=0.25, stream=None,
+                fixed_shape=None):
+        self.plan(v, a, eps, tau128, tau256, stream, fixed_shape)
         self.select(q, k, v, sm_scale, k_abs, k_frac, p, stream)
         return self.attend(sm_scale, stream)
 

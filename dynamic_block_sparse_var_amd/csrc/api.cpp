@@ -187,6 +187,18 @@ prism_status prism_assign_shapes(const prism_problem* pb, const float* g, const 
                               (hipStream_t)stream);
 }
 
+prism_status prism_fixed_shapes(const prism_problem* pb, int32_t shape_index, uint8_t* shape_idx,
+                                int32_t* zone_block_off, int32_t* block_start, void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(shape_idx, "shape_idx"));
+  PRISM_TRY(need_aligned(zone_block_off, "zone_block_off"));
+  PRISM_TRY(need_aligned(block_start, "block_start"));
+  if (shape_index < 0 || shape_index > 15) return fail(PRISM_E_RANGE, "shape_index = %d not in [0, 15]", shape_index);
+  Geom gm = make_geom(pb);
+  return launch_fixed_shapes(gm, shape_index, shape_idx, zone_block_off, block_start, (hipStream_t)stream);
+}
+
 prism_status prism_permute(const prism_problem* pb, const uint8_t* shape_idx, int32_t inverse, int32_t count,
                            const void* const* src, void* const* dst, void* stream) {
   g_err[0] = 0;

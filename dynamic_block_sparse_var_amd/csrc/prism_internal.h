@@ -99,6 +99,8 @@ prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, flo
 prism_status launch_assign_shapes(const Geom& g, const float* gin, const float* rho, float tau128,
                                   float tau256, uint8_t* shape_idx, int32_t* zone_block_off,
                                   int32_t* block_start, hipStream_t st);
+prism_status launch_fixed_shapes(const Geom& g, int shape_index, uint8_t* shape_idx, int32_t* zone_block_off,
+                                 int32_t* block_start, hipStream_t st);
 prism_status launch_permute(const Geom& g, const uint8_t* shape_idx, int inverse, int count,
                             const void* const* src, void* const* dst, hipStream_t st);
 prism_status launch_pool(const Geom& g, const int32_t* block_start, int count,

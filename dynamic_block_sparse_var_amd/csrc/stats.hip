@@ -255,6 +255,25 @@ __global__ __launch_bounds__(1024) void k_assign_shapes(const float* __restrict_
   for (int j = total + threadIdx.x; j <= nbmax; j += 1024) bs[j] = N;
 }
 
+// One shape for every zone: zone m owns blocks [m * nb, (m + 1) * nb) with nb = 512 / B.
+__global__ __launch_bounds__(256) void k_fixed_shapes(int shape_index, uint8_t* __restrict__ shape_idx,
+                                                      int32_t* __restrict__ zone_block_off,
+                                                      int32_t* __restrict__ block_start, int Z, int nbmax, int N) {
+  const int grp = blockIdx.y;
+  const int B = c_shapes[shape_index].vol;
+  const int nb = kZoneVol / B;
+  int32_t* zbo = zone_block_off + (int64_t)grp * (Z + 1);
+  int32_t* bs = block_start + (int64_t)grp * (nbmax + 1);
+  for (int m = blockIdx.x * 256 + threadIdx.x; m <= Z; m += gridDim.x * 256) {
+    zbo[m] = m * nb;
+    if (m < Z) {
+      shape_idx[(int64_t)grp * Z + m] = (uint8_t)shape_index;
+      for (int b = 0; b < nb; ++b) bs[m * nb + b] = kZoneVol * m + b * B;
+    }
+  }
+  for (int j = Z * nb + blockIdx.x * 256 + threadIdx.x; j <= nbmax; j += gridDim.x * 256) bs[j] = N;
+}
+
 }  // namespace
 
 prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, float eps, float* gout, float* rho,
@@ -283,6 +302,14 @@ prism_status launch_assign_shapes(const Geom& g, const float* gin, const float* 
   hipLaunchKernelGGL(k_assign_shapes, dim3(g.groups), dim3(1024), 0, st, gin, rho, tau128, tau256, shape_idx,
                      zone_block_off, block_start, g.Z, g.nbmax, (int)g.N);
   return check_launch("k_assign_shapes");
+}
+
+prism_status launch_fixed_shapes(const Geom& g, int shape_index, uint8_t* shape_idx, int32_t* zone_block_off,
+                                 int32_t* block_start, hipStream_t st) {
+  dim3 grid((unsigned)((g.Z + 256) / 256), g.groups);
+  hipLaunchKernelGGL(k_fixed_shapes, grid, dim3(256), 0, st, shape_index, shape_idx, zone_block_off, block_start,
+                     g.Z, g.nbmax, (int)g.N);
+  return check_launch("k_fixed_shapes");
 }
 
 }  // namespace prism

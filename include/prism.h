@@ -110,6 +110,15 @@ prism_status prism_assign_shapes(const prism_problem* pb, const float* g, const 
                                  float tau128, float tau256, uint8_t* shape_idx,
                                  int32_t* zone_block_off, int32_t* block_start, void* stream);
 
+/* ---- a2 alternative: one fixed shape for every zone ---------------------------------- *
+ * The pages' ablation with dynamic block shapes switched off (README "Core training
+ * parameters": enable_ivpq_dynamic_block = false uses fixed 4x4x4 blocks; RG "Key ideas"
+ * contrasts it with the adaptive shapes): every zone of every group gets candidate
+ * shape_index (0..15, an index into prism_shape_table; 3 is 4x4x4), so a1 and a2 are skipped.
+ * Outputs as for prism_assign_shapes.  Errors: PRISM_E_RANGE for an index outside 0..15. */
+prism_status prism_fixed_shapes(const prism_problem* pb, int32_t shape_index, uint8_t* shape_idx,
+                                int32_t* zone_block_off, int32_t* block_start, void* stream);
+
 /* ---- a3: token order <-> block order ------------------------------------------------ *
  * Moves rows between token order [N, heads, head_dim] and block order [heads, N, head_dim]
  * using each group's shape map (the block order described above; the pages ask that each

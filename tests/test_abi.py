@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert P.prism_abi_version() == 1
@@ -81,6 +81,14 @@ def test_scalar_ranges_rejected(L):
     assert L.prism_permute(ctypes.byref(pb), FAKE, 2, 1, arr, arr, None) == 3
     assert L.prism_permute(ctypes.byref(pb), FAKE, 0, 5, arr, arr, None) == 3
     assert L.prism_pool_blocks(ctypes.byref(pb), FAKE, 0, arr, arr, None) == 3
+    assert L.prism_fixed_shapes(ctypes.byref(pb), 16, FAKE, FAKE, FAKE, None) == 3
+    assert L.prism_fixed_shapes(ctypes.byref(pb), -1, FAKE, FAKE, FAKE, None) == 3
+
+
+def test_fixed_shape_index():
+    # the pages' fixed-block ablation uses 4x4x4 blocks
+    assert P.fixed_shape_index((4, 4, 4)) == 3
+    assert P.prism_shape_table()[P.fixed_shape_index((2, 4, 8))] == (2, 4, 8)
 
 
 def test_backward_workspace(L):

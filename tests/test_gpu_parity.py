@@ -189,3 +189,59 @@ def test_all_blocks_is_dense_attention(run):
     v = torch.from_numpy(run.inp["v"]).permute(1, 0, 2)
     ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], scale=c.sm_scale)[0]
     assert_close_attn("dense O", f64(L.o), ref.permute(1, 0, 2).double().numpy())
+
+
+def test_fixed_shapes_path(run):
+    """Fixed 4x4x4 blocks for every zone (the pages' fixed-block ablation): layout exact against
+    the oracle's block order for the same shape map, then permute, pool, selection and the
+    forward on that layout against the oracle."""
+    from dynamic_block_sparse_var_amd import fixed_shape_index, prism_permute
+
+    c, L = run.cfg, run.layer
+    fs = fixed_shape_index((4, 4, 4))
+    run.layer.plan(run.v, run.a, c.eps, c.tau128, c.tau256, fixed_shape=fs)
+    torch.cuda.synchronize()
+    shp = np.full((c.groups, c.Z), fs, np.uint8)
+    pos, bs, nb = oracle.block_layout(c.T, c.H, c.W, shp)
+    assert (L.shape_idx.cpu().numpy() == fs).all()
+    np.testing.assert_array_equal(L.block_start.cpu().numpy(), bs)
+    zbo = L.zone_block_off.cpu().numpy()
+    np.testing.assert_array_equal(zbo[:, -1], nb)
+    np.testing.assert_array_equal(zbo[:, :-1], np.broadcast_to(np.arange(c.Z) * 8, (c.groups, c.Z)))
+    # the rest of the path on this layout
+    run.gpu_select()
+    qp = oracle.permute(run.inp["q"], pos, c.heads)
+    kp = oracle.permute(run.inp["k"], pos, c.heads)
+    np.testing.assert_array_equal(f64(L.qp), qp)
+    qbar = oracle.pool(qp, bs, nb, c.groups)
+    kbar = oracle.pool(kp, bs, nb, c.groups)
+    np.testing.assert_allclose(f64(L.qbar), qbar, rtol=1e-5, atol=1e-5)
+    cnt, idx, info = oracle.select(qbar, kbar, nb, c.groups, c.sm_scale, c.k_abs, c.k_frac, c.p)
+    hard, soft, rows = compare_masks(L.sel_count.cpu().numpy(), L.sel_idx.cpu().numpy(), cnt, idx, info, nb,
+                                     c.groups)
+    say(f"  fixed 4x4x4: {int(nb[0])} blocks, {rows} rows, hard {hard}, near-tie {soft}")
+    assert hard == 0 and soft <= cap(rows)
+    L.sel_count.copy_(torch.from_numpy(cnt))
+    L.sel_idx.copy_(torch.from_numpy(idx))
+    L.attend(c.sm_scale)
+    torch.cuda.synchronize()
+    vp = oracle.permute(run.inp["v"], pos, c.heads)
+    of, lf = oracle.attn_fwd(qp, kp, vp, bs, nb, c.groups, cnt, idx, c.sm_scale)
+    assert_close_attn("O (fixed shapes)", f64(L.o), oracle.unpermute(of, pos, c.heads))
+    assert np.abs(L.lse.cpu().numpy().astype(np.float64) - lf).max() <= LSE_ABS
+
+
+def test_dense_selection_through_select(run):
+    """k = N_b through the selection kernel itself selects every block, in order (the dense
+    baseline runs the same kernels with this selection)."""
+    c, o, L = run.cfg, run.orc, run.layer
+    run.inject_oracle_plan()
+    L.select(run.q, run.k, run.v, c.sm_scale, c.nbmax, 0.0, c.p)
+    torch.cuda.synchronize()
+    nb = o["nblocks"]
+    hpg = c.heads // c.groups
+    cnt, idx = L.sel_count.cpu().numpy(), L.sel_idx.cpu().numpy()
+    for h in range(c.heads):
+        n = int(nb[h // hpg])
+        assert (cnt[h, :n] == n).all() and (cnt[h, n:] == 0).all()
+        np.testing.assert_array_equal(idx[h, :n, :n], np.broadcast_to(np.arange(n), (n, n)))
