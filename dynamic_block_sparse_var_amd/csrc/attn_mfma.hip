@@ -683,8 +683,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 
   MaskTiles it;
   it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw);
-  uint32_t doff[Tile<D>::NI], taq[2];
-  dma_offsets<D>(w, lane, doff);
+  uint32_t taq[2];
   tr_table<D>(smem, lane, 32 * qh, taq);
   // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * qh + l32) ^ ((CH * half) << 4);
@@ -696,9 +695,16 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   // 0-15 fetching the 256 bytes (the other lanes repeat them)
   const float* ldsrc = (w == 0) ? L2h : Dh;
   auto stage = [&](uint32_t soff, int stg) __attribute__((always_inline)) {
+    // the load offsets are recomputed here rather than kept live through the loop: this
+    // kernel is at its register limit, and a spill reload inside the loop would make the
+    // compiler wait for the loads just issued
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint32_t doff[Tile<D>::NI];
+    dma_offsets<D>(w, ln, doff);
     uint16_t* s = smem + soff / 2;
     if (w < 2)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(ldsrc + it.rt + 4 * (lane & 15)),
+      __builtin_amdgcn_global_load_lds((gbl_void*)(ldsrc + it.rt + 4 * (ln & 15)),
                                        (lds_void*)(sld + 512 * stg + 256 * w), 16, 0, 0);
     dma_tile<D>(Q + hoff + (int64_t)it.rt * D, s, w, doff);
     dma_tile<D>(dO + hoff + (int64_t)it.rt * D, s + T, w, doff);
