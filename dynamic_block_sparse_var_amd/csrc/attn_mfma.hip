@@ -293,38 +293,60 @@ struct ListTiles {
 };
 
 // Walks the 64-row tiles of the query blocks whose bit is set in a transposed-selection row
-// (wave-uniform state, scalar loads).
+// (wave-uniform state).  64 words of the row are fetched at a time, one per lane, with a ballot
+// of the non-zero ones, so finding the next set bit costs no memory round trip inside a batch
+// and zero words are skipped at once.
 struct MaskTiles {
   const uint32_t* mrow;
   const int32_t* bs;
-  int nw, wi, rt, rend;
-  uint32_t bits;
-  __device__ void advance_block() {
-    while (true) {
-      while (bits == 0u) {
-        if (++wi >= nw) return;
-        bits = mrow[wi];
-      }
-      const int qb = (wi << 5) + __ffs(bits) - 1;
-      bits &= bits - 1;
-      rt = bs[qb];
-      rend = bs[qb + 1];
-      return;
-    }
+  int nw, base, k, rt, rend;
+  uint32_t bits;  // bits of word base + k not yet visited
+  uint32_t w_l;   // per lane: word base + lane
+  uint64_t nz;    // lanes whose word is non-zero
+  __device__ void fetch(int lane) {
+    const int i = base + lane;
+    w_l = (i < nw) ? mrow[i] : 0u;
+    nz = __ballot(w_l != 0u);
   }
-  __device__ void begin(const uint32_t* m, const int32_t* b, int n) {
+  // moves to the first non-zero word among the lanes in rest, or past the row
+  __device__ void seek(int lane, uint64_t rest) {
+    while (rest == 0ull) {
+      base += 64;
+      if (base >= nw) return;
+      fetch(lane);
+      rest = nz;
+    }
+    k = __builtin_ctzll(rest);
+    bits = __builtin_amdgcn_readlane(w_l, k);
+  }
+  __device__ void advance_block(int lane) {
+    if (bits == 0u) {
+      seek(lane, (k >= 63) ? 0ull : nz & (~0ull << (k + 1)));
+      if (base >= nw) return;
+    }
+    const int bit = __builtin_ctz(bits);
+    bits &= bits - 1;
+    const int qb = ((base + k) << 5) + bit;
+    rt = bs[qb];
+    rend = bs[qb + 1];
+  }
+  __device__ void begin(const uint32_t* m, const int32_t* b, int n, int lane) {
     mrow = m;
     bs = b;
     nw = n;
-    wi = 0;
+    base = 0;
+    k = -1;
+    bits = 0u;
     rt = rend = 0;
-    bits = (nw > 0) ? mrow[0] : 0u;
-    if (nw > 0) advance_block();
+    if (nw > 0) {
+      fetch(lane);
+      advance_block(lane);
+    }
   }
-  __device__ bool valid() const { return wi < nw; }
-  __device__ void next(int) {
+  __device__ bool valid() const { return base < nw; }
+  __device__ void next(int lane) {
     rt += 64;
-    if (rt >= rend) advance_block();
+    if (rt >= rend) advance_block(lane);
   }
 };
 
@@ -682,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   }
 
   MaskTiles it;
-  it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw);
+  it.begin(mask_t + ((int64_t)h * nbmax + kb_idx) * nw, bs, nw, lane);
   uint32_t taq[2];
   tr_table<D>(smem, lane, 32 * qh, taq);
   // per-lane read addresses of the stage being computed (moved to the other stage per tile)
