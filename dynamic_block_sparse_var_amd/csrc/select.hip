@@ -4,11 +4,15 @@
 // GEMM (64 x 64 output tiles, 16-deep LDS slabs, 4 x 4 outputs per thread, sequential fp32
 // FMA over the head dimension).  The matrix is written into the caller's sel_idx array (same
 // [heads, NBMAX, NBMAX] 4-byte footprint), row by row.
-// k_select: one 1024-thread workgroup per (query block, head).  It reads its score row into
-// LDS as 64-bit keys (order-preserving score bits << 32 | ~index), bitonic-sorts them in
-// descending order (ties -> lower index first), takes exp(s - s_max) in sorted order, a
-// deterministic block prefix sum for the Top-p cut, then marks the first max(k, n_p) blocks in
-// an LDS bitmap and compacts them in ascending index order into the same row.
+// k_select: one 256-thread workgroup per (query block, head).  Thread t holds the row's entries
+// j = t + 256q (q < 32) as order-preserving 32-bit score keys and their exp(s - s_max).  The
+// order of the attended-set equation (score descending, block index ascending on ties) is never
+// materialised: the two cuts are found by bisection over the key space, both in the same loop --
+// the k-th largest key (counts from wave ballots) and the largest key whose upper set holds at
+// least p of the probability mass (fp64 sums in a fixed order, so the result is deterministic and
+// p = 1 reaches the total exactly).  Entries equal to the cut key are taken in block-index order,
+// then the first max(k, n_p) entries are marked in an LDS bitmap (one ballot per 64 entries) and
+// compacted in ascending index order into the same row.
 #include <math.h>
 
 #include "prism_internal.h"
@@ -76,14 +80,34 @@ __device__ __forceinline__ float unord_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-__global__ __launch_bounds__(1024) void k_select(int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
-                                                 const int32_t* __restrict__ block_start, int nbmax, int hpg, int N,
-                                                 int k_abs, double k_frac, float p) {
-  extern __shared__ uint64_t keys[];  // [P2], later reused as the selection bitmap
-  __shared__ float wtot[16];
-  __shared__ int wcnt[16];
-  __shared__ int np_min;
+constexpr int kSelThreads = 256;
+constexpr int kSelPer = kSelMaxKeys / kSelThreads;  // entries per thread
+
+// inclusive scan over the 256 threads of a workgroup (fixed order); part = [4] scratch
+__device__ __forceinline__ int block_incl_scan(int v, int* part) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) part[wv] = v;
+  __syncthreads();
+  for (int q = 0; q < wv; ++q) v += part[q];
+  __syncthreads();
+  return v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
+                                                        const int32_t* __restrict__ block_start, int nbmax, int hpg,
+                                                        int N, int k_abs, double k_frac, double p) {
+  __shared__ uint32_t sel_bits[kSelMaxKeys / 32], tie_bits[kSelMaxKeys / 32];
+  __shared__ uint32_t red_max[4];
+  __shared__ uint32_t red_u[2][4][2];  // per-wave counts, double-buffered across rounds
+  __shared__ double red_d[2][4];
+  __shared__ int part[4];
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int64_t row = (int64_t)h * nbmax + i;
   if (bs[i] >= N) {
@@ -91,114 +115,148 @@ __global__ __launch_bounds__(1024) void k_select(int32_t* __restrict__ sel_idx, 
     return;
   }
   // number of blocks of this group: first j with bs[j] >= N
-  int lo = 0, hi = nbmax;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (bs[mid] < N) lo = mid + 1; else hi = mid;
+  int lo_b = 0, hi_b = nbmax;
+  while (lo_b < hi_b) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (bs[mid] < N) lo_b = mid + 1; else hi_b = mid;
   }
-  const int nb = lo;
-  int P2 = 1;
-  while (P2 < nb) P2 <<= 1;
+  const int nb = lo_b;
   int32_t* rowp = sel_idx + row * nbmax;
   const float* srow = reinterpret_cast<const float*>(rowp);
-  for (int j = tid; j < P2; j += 1024)
-    keys[j] = (j < nb) ? (((uint64_t)ord_bits(srow[j]) << 32) | (uint32_t)(~(uint32_t)j)) : 0ull;
-  if (tid == 0) np_min = nb;
+
+  // keys (0 marks an entry past the row: every finite score has a key >= 1) and the row max
+  uint32_t u[kSelPer];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q) {
+    const int j = tid + kSelThreads * q;
+    u[q] = (j < nb) ? ord_bits(srow[j]) : 0u;
+    mx = max(mx, u[q]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if (lane == 0) red_max[wv] = mx;
   __syncthreads();
-  // bitonic sort, descending
-  for (int size = 2; size <= P2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (P2 >> 1); t += 1024) {
-        const int a = 2 * t - (t & (stride - 1));
-        const int b = a + stride;
-        const uint64_t ka = keys[a], kb = keys[b];
-        const bool desc = (a & size) == 0;
-        if ((ka < kb) == desc) {
-          keys[a] = kb;
-          keys[b] = ka;
-        }
-      }
-      __syncthreads();
+  mx = max(max(red_max[0], red_max[1]), max(red_max[2], red_max[3]));
+  const float smax = unord_bits(mx);
+  float e[kSelPer];
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q) e[q] = u[q] ? expf(unord_bits(u[q]) - smax) : 0.f;
+
+  // count and mass of the entries with key >= v (block totals, the same for every thread)
+  auto count_ge = [&](uint32_t v) __attribute__((always_inline)) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) c += __popcll(__ballot(u[q] >= v));
+    return c;
+  };
+  auto mass_ge = [&](uint32_t v) __attribute__((always_inline)) {
+    double m = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSelPer; ++q) {
+      float x = e[q];
+      asm volatile("" : "+v"(x));  // widen here, not once for all rounds (64 more registers)
+      m += (u[q] >= v) ? (double)x : 0.0;
     }
-  }
-  // exp(s - s_max) in sorted order, segmented prefix sums (thread t owns [t*CH, t*CH + CH))
-  const float smax = unord_bits((uint32_t)(keys[0] >> 32));
-  const int CH = (P2 + 1023) / 1024;
-  const int r0 = tid * CH;
-  float lsum = 0.f;
-  for (int r = r0; r < r0 + CH && r < nb; ++r) lsum += expf(unord_bits((uint32_t)(keys[r] >> 32)) - smax);
-  // block exclusive scan of lsum (fixed order)
-  const int lane = tid & 63, wv = tid >> 6;
-  float incl = lsum;
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wtot[wv] = incl;
-  __syncthreads();
-  float before = 0.f, total = 0.f;
-  for (int q = 0; q < 16; ++q) {
-    if (q < wv) before += wtot[q];
-    total += wtot[q];
-  }
-  before += incl - lsum;
-  const float target = p * total;
-  if (p > 0.f) {
-    float run = before;
-    for (int r = r0; r < r0 + CH && r < nb; ++r) {
-      run += expf(unord_bits((uint32_t)(keys[r] >> 32)) - smax);
-      if (run >= target) {
-        atomicMin(&np_min, r + 1);
-        break;
-      }
-    }
-  } else if (tid == 0) {
-    np_min = 0;
-  }
-  __syncthreads();
-  const int n_p = np_min;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m += __shfl_xor(m, o, 64);
+    return m;
+  };
+
   long long kk = (k_abs > 0) ? (long long)k_abs : (long long)ceil(k_frac * (double)nb);
   if (kk < 1) kk = 1;
   if (kk > nb) kk = nb;
-  const int nsel = (n_p > (int)kk) ? n_p : (int)kk;
-  // take this thread's selected block indices out of the key array, then reuse it as a bitmap
-  uint32_t myj[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = r0 + u;
-    myj[u] = (u < CH && r < nsel) ? ~(uint32_t)(keys[r] & 0xffffffffull) : 0xffffffffu;
-  }
-  __syncthreads();
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(keys);  // NW words fit in the P2 keys
-  const int NW = (nb + 31) >> 5;
-  for (int w = tid; w < NW; w += 1024) bitmap[w] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (myj[u] != 0xffffffffu) atomicOr(&bitmap[myj[u] >> 5], 1u << (myj[u] & 31));
-  __syncthreads();
-  // ascending compaction: thread t owns bitmap words [t*WPT, t*WPT + WPT)
-  const int WPT = (NW + 1023) / 1024;
-  int c = 0;
-  for (int w = tid * WPT; w < tid * WPT + WPT && w < NW; ++w) c += __popc(bitmap[w]);
-  int ci = c;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(ci, o, 64);
-    if (lane >= o) ci += y;
-  }
-  if (lane == 63) wcnt[wv] = ci;
-  __syncthreads();
-  int pos = ci - c;
-  for (int q = 0; q < wv; ++q) pos += wcnt[q];
-  for (int w = tid * WPT; w < tid * WPT + WPT && w < NW; ++w) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      rowp[pos++] = (w << 5) + b;
+  const uint32_t k = (uint32_t)kk;
+  // Bisection invariants: count(>= lk) >= k > count(>= hk); mass(>= lp) >= target > mass(>= hp).
+  // The first round evaluates key 1 (every entry) to get the total mass with the same
+  // arithmetic as every later round.
+  uint32_t lk = 1u, hk = mx + 1u, lp = 1u, hp = mx + 1u;
+  uint32_t cgt_k = 0u, cgt_p = 0u, cge_p = (uint32_t)nb;
+  double mgt_p = 0.0, total = 0.0, target = 0.0;
+  const bool use_p = p > 0.0;
+  int it = 0;
+  for (bool first = true;; first = false, ++it) {
+    const bool run_k = hk - lk > 1u, run_p = use_p && (first || hp - lp > 1u);
+    if (!run_k && !run_p) break;
+    const uint32_t mk = lk + (hk - lk) / 2u;
+    const uint32_t mp = first ? 1u : lp + (hp - lp) / 2u;
+    const uint32_t ck = run_k ? count_ge(mk) : 0u;
+    const uint32_t cp = run_p ? count_ge(mp) : 0u;
+    const double m = run_p ? mass_ge(mp) : 0.0;
+    const int sl = it & 1;
+    if (lane == 0) {
+      red_u[sl][wv][0] = ck;
+      red_u[sl][wv][1] = cp;
+      red_d[sl][wv] = m;
+    }
+    __syncthreads();
+    const uint32_t CK = red_u[sl][0][0] + red_u[sl][1][0] + red_u[sl][2][0] + red_u[sl][3][0];
+    const uint32_t CP = red_u[sl][0][1] + red_u[sl][1][1] + red_u[sl][2][1] + red_u[sl][3][1];
+    const double M = ((red_d[sl][0] + red_d[sl][1]) + red_d[sl][2]) + red_d[sl][3];
+    if (run_k) {
+      if (CK >= k) lk = mk; else { hk = mk; cgt_k = CK; }
+    }
+    if (run_p) {
+      if (first) {
+        total = M;
+        target = p * total;
+      } else if (M >= target) {
+        lp = mp;
+        cge_p = CP;
+      } else {
+        hp = mp;
+        cgt_p = CP;
+        mgt_p = M;
+      }
     }
   }
-  if (tid == 0) sel_count[row] = nsel;
+  // Top-p: the entries above lp hold less than the target; the tied entries at lp (equal
+  // scores, equal exp) are taken in index order until the target is reached
+  uint32_t n_p = 0u;
+  if (use_p) {
+    const double es = (double)expf(unord_bits(lp) - smax);
+    double t = ceil((target - mgt_p) / es);
+    const double ties = (double)(cge_p - cgt_p);
+    if (t < 1.0) t = 1.0;
+    if (t > ties) t = ties;
+    n_p = cgt_p + (uint32_t)t;
+  }
+  const uint32_t nsel = max(k, n_p);
+  const uint32_t vcut = (n_p > k) ? lp : lk;
+  const uint32_t tneed = nsel - ((n_p > k) ? cgt_p : cgt_k);  // tied entries to take
+
+  // bitmaps of the entries above the cut and at the cut (word w covers entries 32w..32w+31)
+#pragma unroll
+  for (int q = 0; q < kSelPer; ++q) {
+    const uint64_t above = __ballot(u[q] > vcut), at = __ballot(u[q] == vcut);
+    if (lane == 0) {
+      const int w = 2 * wv + 8 * q;
+      sel_bits[w] = (uint32_t)above;
+      sel_bits[w + 1] = (uint32_t)(above >> 32);
+      tie_bits[w] = (uint32_t)at;
+      tie_bits[w + 1] = (uint32_t)(at >> 32);
+    }
+  }
+  __syncthreads();
+  // thread t owns word t: the tied entries of rank < tneed (in index order) join the selection
+  uint32_t tw = tie_bits[tid], sw = sel_bits[tid];
+  const int tc = __popc(tw);
+  int trank = block_incl_scan(tc, part) - tc;
+  while (tw) {
+    const uint32_t b = tw & (0u - tw);
+    tw ^= b;
+    if ((uint32_t)trank < tneed) sw |= b;
+    ++trank;
+  }
+  // ascending compaction
+  const int c = __popc(sw);
+  int pos = block_incl_scan(c, part) - c;
+  while (sw) {
+    const int b = __builtin_ctz(sw);
+    sw &= sw - 1u;
+    rowp[pos++] = (tid << 5) + b;
+  }
+  if (tid == 0) sel_count[row] = (int32_t)nsel;
 }
 
 }  // namespace
@@ -216,12 +274,9 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
   }
   prism_status s = check_launch("k_scores");
   if (s != PRISM_OK) return s;
-  int P2 = 1;
-  while (P2 < g.nbmax) P2 <<= 1;
-  const size_t lds = (size_t)P2 * sizeof(uint64_t);
   KernelTrace tr("k_select", st);
-  hipLaunchKernelGGL(k_select, dim3(g.nbmax, g.heads), dim3(1024), lds, st, sel_idx, sel_count, block_start, g.nbmax,
-                     g.hpg, (int)g.N, k_abs, k_frac, (float)p);
+  hipLaunchKernelGGL(k_select, dim3(g.nbmax, g.heads), dim3(kSelThreads), 0, st, sel_idx, sel_count, block_start,
+                     g.nbmax, g.hpg, (int)g.N, k_abs, k_frac, p);
   return check_launch("k_select");
 }
 
