@@ -167,59 +167,69 @@ __global__ __launch_bounds__(kSelThreads) void k_select(int32_t* __restrict__ se
   if (kk < 1) kk = 1;
   if (kk > nb) kk = nb;
   const uint32_t k = (uint32_t)kk;
-  // Bisection invariants: count(>= lk) >= k > count(>= hk); mass(>= lp) >= target > mass(>= hp).
-  // The first round evaluates key 1 (every entry) to get the total mass with the same
-  // arithmetic as every later round.
-  uint32_t lk = 1u, hk = mx + 1u, lp = 1u, hp = mx + 1u;
-  uint32_t cgt_k = 0u, cgt_p = 0u, cge_p = (uint32_t)nb;
-  double mgt_p = 0.0, total = 0.0, target = 0.0;
-  const bool use_p = p > 0.0;
-  int it = 0;
-  for (bool first = true;; first = false, ++it) {
-    const bool run_k = hk - lk > 1u, run_p = use_p && (first || hp - lp > 1u);
-    if (!run_k && !run_p) break;
-    const uint32_t mk = lk + (hk - lk) / 2u;
-    const uint32_t mp = first ? 1u : lp + (hp - lp) / 2u;
-    const uint32_t ck = run_k ? count_ge(mk) : 0u;
-    const uint32_t cp = run_p ? count_ge(mp) : 0u;
-    const double m = run_p ? mass_ge(mp) : 0.0;
-    const int sl = it & 1;
-    if (lane == 0) {
-      red_u[sl][wv][0] = ck;
-      red_u[sl][wv][1] = cp;
-      red_d[sl][wv] = m;
-    }
+  // Block totals of per-wave values (fixed order), through LDS slots alternating between
+  // rounds so that one barrier per round suffices.
+  int round = 0;
+  auto reduce_u = [&](uint32_t v) __attribute__((always_inline)) {
+    const int sl = round & 1;
+    if (lane == 0) red_u[sl][wv][0] = v;
     __syncthreads();
-    const uint32_t CK = red_u[sl][0][0] + red_u[sl][1][0] + red_u[sl][2][0] + red_u[sl][3][0];
-    const uint32_t CP = red_u[sl][0][1] + red_u[sl][1][1] + red_u[sl][2][1] + red_u[sl][3][1];
-    const double M = ((red_d[sl][0] + red_d[sl][1]) + red_d[sl][2]) + red_d[sl][3];
-    if (run_k) {
-      if (CK >= k) lk = mk; else { hk = mk; cgt_k = CK; }
-    }
-    if (run_p) {
-      if (first) {
-        total = M;
-        target = p * total;
-      } else if (M >= target) {
-        lp = mp;
-        cge_p = CP;
-      } else {
-        hp = mp;
-        cgt_p = CP;
-        mgt_p = M;
-      }
-    }
+    ++round;
+    return red_u[sl][0][0] + red_u[sl][1][0] + red_u[sl][2][0] + red_u[sl][3][0];
+  };
+  auto reduce_d = [&](double v) __attribute__((always_inline)) {
+    const int sl = round & 1;
+    if (lane == 0) red_d[sl][wv] = v;
+    __syncthreads();
+    ++round;
+    return ((red_d[sl][0] + red_d[sl][1]) + red_d[sl][2]) + red_d[sl][3];
+  };
+  // Top-k cut by bisection over the key space: count(>= lk) >= k > count(>= hk).  lk ends on
+  // the key of the k-th entry; cgt_k = count(> lk).
+  uint32_t lk = 1u, hk = mx + 1u, cgt_k = 0u;
+  while (hk - lk > 1u) {
+    const uint32_t mk = lk + (hk - lk) / 2u;
+    const uint32_t c = reduce_u(count_ge(mk));
+    if (c >= k) lk = mk; else { hk = mk; cgt_k = c; }
   }
-  // Top-p: the entries above lp hold less than the target; the tied entries at lp (equal
-  // scores, equal exp) are taken in index order until the target is reached
-  uint32_t n_p = 0u;
-  if (use_p) {
-    const double es = (double)expf(unord_bits(lp) - smax);
-    double t = ceil((target - mgt_p) / es);
-    const double ties = (double)(cge_p - cgt_p);
-    if (t < 1.0) t = 1.0;
-    if (t > ties) t = ties;
-    n_p = cgt_p + (uint32_t)t;
+  // Top-p: the first k entries (those above lk, then the tied ones at lk in index order, all
+  // with the same exp) are enough unless their mass falls short of p * total; only then is the
+  // Top-p cut searched, below the Top-k cut: mass(>= lp) >= target > mass(>= hp), which makes
+  // lp the key of the entry that reaches the target.
+  uint32_t n_p = 0u, lp = lk, cgt_p = 0u;
+  if (p > 0.0) {
+    const double total = reduce_d(mass_ge(1u));  // the same arithmetic as every mass below
+    const double target = p * total;
+    const double es_k = (double)expf(unord_bits(lk) - smax);
+    double mgt = reduce_d(mass_ge(hk));
+    if (mgt + (double)(k - cgt_k) * es_k >= target) {
+      n_p = k;  // n_p <= k: the Top-k prefix already holds the target mass
+    } else {
+      lp = 1u;
+      uint32_t hp = hk, cge = (uint32_t)nb;
+      cgt_p = cgt_k;
+      while (hp - lp > 1u) {
+        const uint32_t mp = lp + (hp - lp) / 2u;
+        const uint32_t c = reduce_u(count_ge(mp));
+        const double m = reduce_d(mass_ge(mp));
+        if (m >= target) {
+          lp = mp;
+          cge = c;
+        } else {
+          hp = mp;
+          cgt_p = c;
+          mgt = m;
+        }
+      }
+      // the tied entries at lp (equal scores, equal exp) are taken in index order until the
+      // target is reached
+      const double es = (double)expf(unord_bits(lp) - smax);
+      double t = ceil((target - mgt) / es);
+      const double ties = (double)(cge - cgt_p);
+      if (t < 1.0) t = 1.0;
+      if (t > ties) t = ties;
+      n_p = cgt_p + (uint32_t)t;
+    }
   }
   const uint32_t nsel = max(k, n_p);
   const uint32_t vcut = (n_p > k) ? lp : lk;
