@@ -6,8 +6,11 @@ One step = one layer's whole path, forward and backward, on the 2K-shaped token 
 blocks, p = 0.9 (seeded synthetic inputs of that shape; see synth/):
 
   zone statistics -> volume/shape assignment -> permute Q,K,V -> pool Q,K -> select ->
-  sparse attention forward -> unpermute O -> permute dO -> sparse attention backward ->
-  unpermute dQ, dK, dV
+  sparse attention forward (O written in token order) -> sparse attention backward (dO
+  permuted into block order inside; dQ, dK, dV written in token order)
+
+``--block-io`` runs the block-order calls instead, with separate unpermute O / permute dO /
+unpermute gradient passes.
 
 Printed: one JSON line.  ``value`` is ms per layer (whole step, lower is better).  Extra
 fields give per-stage times, attention TFLOP/s on executed (selected-block, algorithmic)
@@ -195,6 +198,8 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a known-size reference "
                          "for hardware byte counters)")
+    ap.add_argument("--block-io", action="store_true",
+                    help="block-order attention calls with separate permutes of O, dO and the gradients")
     ap.add_argument("--dense", action="store_true",
                     help="dense baseline: every key block selected (k = N_b) on the same kernels")
     ap.add_argument("--fixed-shape", action="store_true",
@@ -232,11 +237,13 @@ def main():
     do = torch.from_numpy(inp["dout"]).to(dt).to(dev)
     a = torch.from_numpy(inp["a"]).to(dev)
     pb = P.make_problem(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.groups, cfg.dtype)
-    L = P.PrismLayer(pb, device=dev, backward=True)
+    L = P.PrismLayer(pb, device=dev, backward=True, token_io=not args.block_io)
     pb32 = P.Problem(pb.T, pb.H, pb.W, pb.heads, pb.head_dim, pb.groups, P.F32)
     sm = cfg.sm_scale
     stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
               "permute_do", "bsa_bwd", "unpermute_grads"]
+    if not args.block_io:
+        stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "bsa_bwd"]
 
     fixed = P.fixed_shape_index((4, 4, 4)) if args.fixed_shape else None
     # dense baseline: every key block selected (k = N_b), the same kernels otherwise
@@ -263,6 +270,14 @@ def main():
         P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, k_abs, k_frac, cfg.p, L.sel_count,
                               L.sel_idx)
         mark(5)
+        if not args.block_io:
+            P.prism_bsa_fwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
+                                L.o_lo, L.lse)
+            mark(6)
+            P.prism_bsa_bwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
+                                L.o_lo, do, L.lse, L.dq, L.dk, L.dv, L.workspace)
+            mark(7)
+            return
         P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse)
         mark(6)
         P.prism_permute(pb, L.shape_idx, 1, [L.op], [L.o])
@@ -289,7 +304,7 @@ def main():
     # per-kernel events recorded by the library around its own launches
     kev = {kn: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)] for kn in MFMA_KERNELS + HBM_KERNELS}
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(args.steps)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for st in range(args.steps):  # make every event a live HIP event before timing
         for kn in kev:
@@ -401,6 +416,7 @@ def main():
                                   f"k {cfg.k_frac:.0%} p {cfg.p}, ")
                                + ("fixed 4x4x4 blocks, " if args.fixed_shape else "")
                                + "forward + backward",
+                   "io": "block order + permutes" if args.block_io else "token order",
                    "parallelism": "none (1 GPU)"},
         "attn_fwd_bwd_ms": round(attn_ms, 3),
         "attn_tflops": round(attn_tflops, 1),

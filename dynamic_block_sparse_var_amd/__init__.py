@@ -91,6 +91,10 @@ def lib():
         "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
+        "prism_bsa_fwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "prism_bsa_bwd_tok_workspace_bytes": (ctypes.c_size_t, [_PB]),
+        "prism_bsa_bwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, ctypes.c_size_t, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -193,6 +197,24 @@ def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_l
                                nbytes, _stream(stream)), "prism_bsa_bwd")
 
 
+def prism_bsa_fwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, stream=None):
+    _check(lib().prism_bsa_fwd_tok(ctypes.byref(pb), _p(shape_idx), _p(block_start), _p(sel_count), _p(sel_idx),
+                                   sm_scale, _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(lse), _stream(stream)),
+           "prism_bsa_fwd_tok")
+
+
+def prism_bsa_bwd_tok_workspace_bytes(pb) -> int:
+    return int(lib().prism_bsa_bwd_tok_workspace_bytes(ctypes.byref(pb)))
+
+
+def prism_bsa_bwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, dout, lse, dq, dk,
+                      dv, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().prism_bsa_bwd_tok(ctypes.byref(pb), _p(shape_idx), _p(block_start), _p(sel_count), _p(sel_idx),
+                                   sm_scale, _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk),
+                                   _p(dv), _p(workspace), nbytes, _stream(stream)), "prism_bsa_bwd_tok")
+
+
 def prism_trace_kernel(kernel, start_event=None, stop_event=None):
     """Time one library kernel with two torch.cuda.Event(enable_timing=True) objects
     (kernel=None clears all hooks).  The events must already exist as HIP events, so they
@@ -215,8 +237,11 @@ class PrismLayer:
     zone_block_off, block_start, qp/kp/vp, qbar/kbar, sel_count/sel_idx, op, lse, o, ...),
     which is what the tests inspect.  Allocation happens once, in the constructor."""
 
-    def __init__(self, pb: Problem, device="cuda", backward=False):
+    def __init__(self, pb: Problem, device="cuda", backward=False, token_io=False):
+        """token_io: the attention writes O and the gradients straight to token order
+        (prism_bsa_fwd_tok / prism_bsa_bwd_tok), with no block-order O, dO or gradient buffers."""
         self.pb = pb
+        self.token_io = token_io
         dt = pb.torch_dtype
         N, H_, d, G, Z, NB = pb.N, pb.heads, pb.head_dim, pb.groups, pb.Z, pb.nbmax
         e = dict(device=device)
@@ -233,20 +258,26 @@ class PrismLayer:
         self.kbar = torch.empty_like(self.qbar)
         self.sel_count = torch.empty(H_, NB, dtype=torch.int32, **e)
         self.sel_idx = torch.empty(H_, NB, NB, dtype=torch.int32, **e)
-        self.op = torch.empty_like(self.qp)
-        # rounding residual of O (bf16 only), kept for an accurate backward
-        self.op_lo = torch.empty_like(self.qp) if (backward and pb.dtype == BF16) else None
         self.lse = torch.empty(H_, N, dtype=torch.float32, **e)
         self.o = torch.empty(N, H_, d, dtype=dt, **e)
+        # rounding residual of O (bf16 only), kept for an accurate backward
+        keep_lo = backward and pb.dtype == BF16
+        if token_io:
+            self.op = None
+            self.o_lo = torch.empty_like(self.o) if keep_lo else None
+        else:
+            self.op = torch.empty_like(self.qp)
+            self.op_lo = torch.empty_like(self.qp) if keep_lo else None
         if backward:
-            self.dop = torch.empty_like(self.qp)
-            self.dqp = torch.empty(H_, N, d, dtype=torch.float32, **e)
-            self.dkp = torch.empty_like(self.dqp)
-            self.dvp = torch.empty_like(self.dqp)
+            if not token_io:
+                self.dop = torch.empty_like(self.qp)
+                self.dqp = torch.empty(H_, N, d, dtype=torch.float32, **e)
+                self.dkp = torch.empty_like(self.dqp)
+                self.dvp = torch.empty_like(self.dqp)
             self.dq = torch.empty(N, H_, d, dtype=torch.float32, **e)
             self.dk = torch.empty_like(self.dq)
             self.dv = torch.empty_like(self.dq)
-            nbytes = prism_bsa_bwd_workspace_bytes(pb)
+            nbytes = prism_bsa_bwd_tok_workspace_bytes(pb) if token_io else prism_bsa_bwd_workspace_bytes(pb)
             self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, **e)
 
     # a1..a5
@@ -271,6 +302,10 @@ class PrismLayer:
     # a6
     def attend(self, sm_scale, stream=None):
         pb = self.pb
+        if self.token_io:
+            prism_bsa_fwd_tok(pb, self.shape_idx, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp,
+                              self.kp, self.vp, self.o, self.o_lo, self.lse, stream)
+            return self.o
         prism_bsa_fwd(pb, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp, self.kp, self.vp,
                       self.op, self.op_lo, self.lse, stream)
         prism_permute(pb, self.shape_idx, 1, [self.op], [self.o], stream)
@@ -285,6 +320,11 @@ class PrismLayer:
     # a7
     def backward(self, dout, sm_scale, stream=None):
         pb = self.pb
+        if self.token_io:
+            prism_bsa_bwd_tok(pb, self.shape_idx, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp,
+                              self.kp, self.vp, self.o, self.o_lo, dout, self.lse, self.dq, self.dk, self.dv,
+                              self.workspace, stream)
+            return self.dq, self.dk, self.dv
         prism_permute(pb, self.shape_idx, 0, [dout], [self.dop], stream)
         prism_bsa_bwd(pb, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp, self.kp, self.vp,
                       self.op, self.op_lo, self.dop, self.lse, self.dqp, self.dkp, self.dvp, self.workspace, stream)
@@ -300,7 +340,7 @@ class PrismAttentionFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, a, pb, sm_scale, k_abs, k_frac, p):
-        layer = PrismLayer(pb, device=q.device, backward=True)
+        layer = PrismLayer(pb, device=q.device, backward=True, token_io=True)
         o = layer.forward(q.contiguous(), k.contiguous(), v.contiguous(), a, sm_scale, k_abs, k_frac, p)
         ctx.layer, ctx.sm_scale = layer, sm_scale
         return o.clone()

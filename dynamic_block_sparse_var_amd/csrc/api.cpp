@@ -269,7 +269,7 @@ prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start, 
     return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
   Geom gm = make_geom(pb);
   return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, lse,
-                        (hipStream_t)stream);
+                        block_rows(), (hipStream_t)stream);
 }
 
 size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb) {
@@ -306,7 +306,78 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, 
   if (workspace_bytes < need)
     return fail(PRISM_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   return launch_bsa_bwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, dout,
-                        lse, dq, dk, dv, workspace, (hipStream_t)stream);
+                        lse, dq, dk, dv, workspace, block_rows(), block_rows(), (hipStream_t)stream);
+}
+
+// ---- token-order interface of the attention ---------------------------------------------
+
+prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
+                               const int32_t* sel_count, const int32_t* sel_idx, float sm_scale, const void* q,
+                               const void* k, const void* v, void* o, void* o_lo, float* lse, void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(shape_idx, "shape_idx"));
+  PRISM_TRY(need_aligned(block_start, "block_start"));
+  PRISM_TRY(need_aligned(sel_count, "sel_count"));
+  PRISM_TRY(need_aligned(sel_idx, "sel_idx"));
+  PRISM_TRY(need_aligned(q, "q"));
+  PRISM_TRY(need_aligned(k, "k"));
+  PRISM_TRY(need_aligned(v, "v"));
+  PRISM_TRY(need_aligned(o, "o"));
+  if (o_lo) PRISM_TRY(need_aligned(o_lo, "o_lo"));
+  PRISM_TRY(need_aligned(lse, "lse"));
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
+  Geom gm = make_geom(pb);
+  return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, lse,
+                        token_rows(gm, shape_idx), (hipStream_t)stream);
+}
+
+// the block-order backward workspace, then a block-order copy of dO
+static size_t dout_copy_offset(const Geom& gm) { return (bsa_bwd_workspace_bytes(gm) + 255) & ~(size_t)255; }
+
+size_t prism_bsa_bwd_tok_workspace_bytes(const prism_problem* pb) {
+  if (validate_problem(pb) != PRISM_OK) return 0;
+  Geom gm = make_geom(pb);
+  return dout_copy_offset(gm) + (size_t)gm.heads * (size_t)gm.N * (size_t)gm.d * (size_t)gm.esize;
+}
+
+prism_status prism_bsa_bwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
+                               const int32_t* sel_count, const int32_t* sel_idx, float sm_scale, const void* q,
+                               const void* k, const void* v, const void* o, const void* o_lo, const void* dout,
+                               const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(shape_idx, "shape_idx"));
+  PRISM_TRY(need_aligned(block_start, "block_start"));
+  PRISM_TRY(need_aligned(sel_count, "sel_count"));
+  PRISM_TRY(need_aligned(sel_idx, "sel_idx"));
+  PRISM_TRY(need_aligned(q, "q"));
+  PRISM_TRY(need_aligned(k, "k"));
+  PRISM_TRY(need_aligned(v, "v"));
+  PRISM_TRY(need_aligned(o, "o"));
+  if (o_lo) PRISM_TRY(need_aligned(o_lo, "o_lo"));
+  PRISM_TRY(need_aligned(dout, "dout"));
+  PRISM_TRY(need_aligned(lse, "lse"));
+  PRISM_TRY(need_aligned(dq, "dq"));
+  PRISM_TRY(need_aligned(dk, "dk"));
+  PRISM_TRY(need_aligned(dv, "dv"));
+  PRISM_TRY(need_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PRISM_E_ALIGN, "workspace not 256-byte aligned");
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
+  Geom gm = make_geom(pb);
+  const size_t need = prism_bsa_bwd_tok_workspace_bytes(pb);
+  if (workspace_bytes < need)
+    return fail(PRISM_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  void* dout_p = static_cast<uint8_t*>(workspace) + dout_copy_offset(gm);
+  const void* src[1] = {dout};
+  void* dst[1] = {dout_p};
+  PRISM_TRY(launch_permute(gm, shape_idx, 0, 1, src, dst, (hipStream_t)stream));
+  const RowMap tok = token_rows(gm, shape_idx);
+  return launch_bsa_bwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, dout_p,
+                        lse, dq, dk, dv, workspace, tok, tok, (hipStream_t)stream);
 }
 
 }  // extern "C"

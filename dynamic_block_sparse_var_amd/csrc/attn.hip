@@ -18,6 +18,8 @@ namespace prism {
 
 namespace {
 
+PRISM_DEVICE_SHAPES
+
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i);
 template <>
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(64) void k_ref_fwd(const T* __restrict__ q, const T
                                                 const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int64_t N,
-                                                float sm_scale) {
+                                                float sm_scale, RowMap rm) {
   const int h = blockIdx.y;
   const int row = blockIdx.x * 64 + threadIdx.x;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
@@ -69,8 +71,9 @@ __global__ __launch_bounds__(64) void k_ref_fwd(const T* __restrict__ q, const T
     }
   }
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const int64_t orow = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, row);
 #pragma unroll
-  for (int e = 0; e < D; ++e) st(o, (hb + row) * D + e, acc[e] * inv);
+  for (int e = 0; e < D; ++e) st(o, orow * D + e, acc[e] * inv);
   lse[hb + row] = (l > 0.f) ? m + logf(l) : -INFINITY;
 }
 
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(64) void k_ref_dq(const T* __restrict__ q, const T*
                                                float* __restrict__ dq, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int64_t N,
-                                               float sm_scale) {
+                                               float sm_scale, RowMap rm) {
   const int h = blockIdx.y;
   const int row = blockIdx.x * 64 + threadIdx.x;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(64) void k_ref_dq(const T* __restrict__ q, const T*
       for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, ld(k, (hb + c) * D + e), acc[e]);
     }
   }
+  const int64_t orow = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, row);
 #pragma unroll
-  for (int e = 0; e < D; ++e) dq[(hb + row) * D + e] = acc[e] * sm_scale;
+  for (int e = 0; e < D; ++e) dq[orow * D + e] = acc[e] * sm_scale;
 }
 
 template <typename T, int D>
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const 
                                                  float* __restrict__ dk, float* __restrict__ dv,
                                                  const int32_t* __restrict__ block_start,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
-                                                 int64_t N, float sm_scale) {
+                                                 int64_t N, float sm_scale, RowMap rm) {
   const int h = blockIdx.y;
   const int key = blockIdx.x * 64 + threadIdx.x;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
@@ -159,10 +163,11 @@ __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const 
       }
     }
   }
+  const int64_t krow = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, key);
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    dk[(hb + key) * D + e] = adk[e] * sm_scale;
-    dv[(hb + key) * D + e] = adv[e];
+    dk[krow * D + e] = adk[e] * sm_scale;
+    dv[krow * D + e] = adv[e];
   }
 }
 
@@ -188,12 +193,14 @@ __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, c
 }
 
 // delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step.  O = o + o_lo when the
-// forward stored its rounding residual.  Also lse2 = LSE * log2(e), the row statistic in the
-// base-2 units the matrix-core backward uses.
+// forward stored its rounding residual; o and o_lo are read in block or token order (om), dO in
+// block order.  Also lse2 = LSE * log2(e), the row statistic in the base-2 units the
+// matrix-core backward uses.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T* __restrict__ olo,
                                                const T* __restrict__ dout, const float* __restrict__ lse,
-                                               float* __restrict__ delta, float* __restrict__ lse2, int64_t rows) {
+                                               float* __restrict__ delta, float* __restrict__ lse2, int64_t rows,
+                                               RowMap om, int hpg, int heads, int64_t N) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int LPR = D / EPC;  // lanes per row (8..32)
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -201,13 +208,15 @@ __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T*
   const int part = (int)(gt % LPR);
   float acc = 0.f;
   if (row < rows) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * EPC);
+    const int h = (int)(row / N);
+    const int64_t orow = out_row(om, c_shapes, h / hpg, h, heads, N, (int)(row - (int64_t)h * N));
+    const uint4 a = *reinterpret_cast<const uint4*>(o + orow * D + part * EPC);
     const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + part * EPC);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
     if constexpr (sizeof(T) == 2) {
       uint32_t wl[4] = {0u, 0u, 0u, 0u};
       if (olo) {
-        const uint4 c = *reinterpret_cast<const uint4*>(olo + row * D + part * EPC);
+        const uint4 c = *reinterpret_cast<const uint4*>(olo + orow * D + part * EPC);
         wl[0] = c.x; wl[1] = c.y; wl[2] = c.z; wl[3] = c.w;
       }
 #pragma unroll
@@ -230,10 +239,11 @@ __global__ __launch_bounds__(256) void k_delta(const T* __restrict__ o, const T*
 
 template <typename T, int D>
 prism_status run_ref_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
-                         const void* q, const void* k, const void* v, void* o, float* lse, hipStream_t st) {
+                         const void* q, const void* k, const void* v, void* o, float* lse, const RowMap& out,
+                         hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   hipLaunchKernelGGL((k_ref_fwd<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, bs,
-                     cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
+                     cnt, idx, g.nbmax, g.hpg, g.N, sm_scale, out);
   return check_launch("k_ref_fwd");
 }
 
@@ -241,14 +251,14 @@ template <typename T, int D>
 prism_status run_ref_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                          const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
-                         hipStream_t st) {
+                         const RowMap& out, hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   hipLaunchKernelGGL((k_ref_dq<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
-                     (const T*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, g.N, sm_scale);
+                     (const T*)dout, lse, delta, dq, bs, cnt, idx, g.nbmax, g.hpg, g.N, sm_scale, out);
   prism_status s = check_launch("k_ref_dq");
   if (s != PRISM_OK) return s;
   hipLaunchKernelGGL((k_ref_dkdv<T, D>), grid, dim3(64), 0, st, (const T*)q, (const T*)k, (const T*)v,
-                     (const T*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw, g.hpg, g.N, sm_scale);
+                     (const T*)dout, lse, delta, dk, dv, bs, mask_t, g.nbmax, nw, g.hpg, g.N, sm_scale, out);
   return check_launch("k_ref_dkdv");
 }
 
@@ -271,16 +281,16 @@ size_t bsa_bwd_workspace_bytes(const Geom& g) { return bwd_workspace_layout(g).t
 
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                             const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
-                            hipStream_t st) {
-  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, o_lo, lse, st);
-  if (g.d == 64) return run_ref_fwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
-  return run_ref_fwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, st);
+                            const RowMap& out, hipStream_t st) {
+  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, o_lo, lse, out, st);
+  if (g.d == 64) return run_ref_fwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, out, st);
+  return run_ref_fwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, out, st);
 }
 
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                             const void* q, const void* k, const void* v, const void* o, const void* o_lo,
                             const void* dout, const float* lse, float* dq, float* dk, float* dv, void* ws,
-                            hipStream_t st) {
+                            const RowMap& o_in, const RowMap& out, hipStream_t st) {
   const BwdWorkspace w = bwd_workspace_layout(g);
   float* delta = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.delta_off);
   float* lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.lse2_off);
@@ -302,25 +312,27 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   if (g.bf16) {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<uint16_t, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows, o_in, g.hpg, g.heads, g.N);
     else
       hipLaunchKernelGGL((k_delta<uint16_t, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const uint16_t*)o,
-                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows);
+                         (const uint16_t*)o_lo, (const uint16_t*)dout, lse, delta, lse2, rows, o_in, g.hpg, g.heads, g.N);
   } else {
     if (g.d == 64)
       hipLaunchKernelGGL((k_delta<float, 64>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows);
+                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows, o_in, g.hpg, g.heads, g.N);
     else
       hipLaunchKernelGGL((k_delta<float, 128>), dim3((unsigned)dblocks), dim3(256), 0, st, (const float*)o,
-                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows);
+                         (const float*)nullptr, (const float*)dout, lse, delta, lse2, rows, o_in, g.hpg, g.heads, g.N);
   }
   s = check_launch("k_delta");
   if (s != PRISM_OK) return s;
   if (g.bf16)
-    return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse2, delta, mask_t, w.nw, dq, dk, dv, st);
+    return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse2, delta, mask_t, w.nw, dq, dk, dv, out, st);
   if (g.d == 64)
-    return run_ref_bwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
-  return run_ref_bwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, st);
+    return run_ref_bwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, out,
+                                  st);
+  return run_ref_bwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, out,
+                                 st);
 }
 
 }  // namespace prism

@@ -16,10 +16,10 @@ BwdWorkspace bwd_workspace_layout(const Geom& g);
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, void* o, void* o_lo,
-                             float* lse, hipStream_t st);
+                             float* lse, const RowMap& out, hipStream_t st);
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, const void* dout,
                              const float* lse2, const float* delta, const uint32_t* mask_t, int nw, float* dq,
-                             float* dk, float* dv, hipStream_t st);
+                             float* dk, float* dv, const RowMap& out, hipStream_t st);
 
 }  // namespace prism

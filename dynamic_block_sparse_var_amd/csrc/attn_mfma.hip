@@ -44,6 +44,8 @@ namespace prism {
 
 namespace {
 
+PRISM_DEVICE_SHAPES
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
                                                 const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
-                                                float scale2) {
+                                                float scale2, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
   constexpr uint32_t SB = 4 * T;  // bytes of one stage (K tile, V tile)
@@ -493,9 +495,10 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     if (half == 0) LSE[(int64_t)h * N + myrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
     // the lane holds O[myrow][d = 32db + 8jj + 4half + e]: O rounded to bf16 and, if requested,
-    // its rounding residual, 8 bytes per lane and store
-    uint16_t* orow = O + hoff + (int64_t)myrow * D + 4 * half;
-    uint16_t* rrow = Olo ? Olo + hoff + (int64_t)myrow * D + 4 * half : nullptr;
+    // its rounding residual, 8 bytes per lane and store, in block or token order
+    const int64_t orw = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, myrow) * D + 4 * half;
+    uint16_t* orow = O + orw;
+    uint16_t* rrow = Olo ? Olo + orw : nullptr;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
                                                float* __restrict__ dQ, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
-                                               float scale2, float sm_scale) {
+                                               float scale2, float sm_scale, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
   constexpr uint32_t SB = 4 * T;  // bytes of one stage (K tile, V tile)
@@ -637,20 +640,34 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
   }
   __syncthreads();
   if (kh == 0) {
-    // fp32 output: lane holds dQ[myrow][32db + 8jj + 4half + e]
-    float* dqr = dQ + hoff + (int64_t)myrow * D + 4 * half;
+    // the lane holds dQ[myrow][32db + 8jj + 4half + e].  The wave's 32 x D block goes out as whole
+    // rows (32 lanes x 16 bytes per row and store): it is staged in the wave's own LDS region
+    // (read out above first), 16-byte chunk c of row r at chunk slot c ^ (r % CPR)
+    constexpr int CPR = D / 4;  // 16-byte chunks per fp32 row
+    float* xs = xo + rh * DB * 16 * 64;
+    float acc[DB][16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = (dqacc[db][r] + xs[(db * 16 + r) * 64 + lane]) * sm_scale;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every lane's partner values are read
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * jj + e;
-          v[e] = (dqacc[db][r] + xo[((rh * DB + db) * 16 + r) * 64 + lane]) * sm_scale;
-        }
-        *reinterpret_cast<float4*>(dqr + 32 * db + 8 * jj) = make_float4(v[0], v[1], v[2], v[3]);
+        const int c = 8 * db + 2 * jj + half;
+        *reinterpret_cast<float4*>(xs + l32 * D + 4 * (c ^ (l32 & (CPR - 1)))) =
+            make_float4(acc[db][4 * jj], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]);
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lane / CPR, c = lane % CPR;
+      const float4 x = *reinterpret_cast<const float4*>(xs + r * D + 4 * (c ^ (r & (CPR - 1))));
+      const int row = row0 + 32 * rh + r;
+      *reinterpret_cast<float4*>(dQ + out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, row) * D + 4 * c) = x;
+    }
   }
 }
 
@@ -668,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
                                                  float* __restrict__ dK, float* __restrict__ dV,
                                                  const int32_t* __restrict__ block_start,
                                                  const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
-                                                 int N, float scale2, float sm_scale) {
+                                                 int N, float scale2, float sm_scale, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
   constexpr uint32_t SB = 4 * T;  // bytes of one stage's tiles (Q, dO)
@@ -835,16 +852,18 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   __syncthreads();
   if (qh == 0) {
     // fp32 outputs: accumulators hold [key = 8jj + 4half + e][d = 32db + l32]; 32 lanes store
-    // 128 contiguous bytes of one key row per instruction
+    // 128 contiguous bytes of one key row per instruction; block or token order
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int64_t krow = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, key) * D + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int64_t off = hoff + (int64_t)key * D + 32 * db + l32;
+      for (int db = 0; db < DB; ++db) {
+        const int64_t off = krow + 32 * db;
         dK[off] = (dkacc[db][r] + xo[(((2 * kh + 0) * DB + db) * 16 + r) * 64 + lane]) * sm_scale;
         dV[off] = dvacc[db][r] + xo[(((2 * kh + 1) * DB + db) * 16 + r) * 64 + lane];
       }
+    }
   }
 }
 
@@ -852,25 +871,25 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
-                             hipStream_t st) {
+                             const RowMap& out, hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   KernelTrace tr("k_fwd", st);
   if (g.d == 64)
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
-                       (int)g.N, scale2);
+                       (int)g.N, scale2, out);
   else
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
-                       (int)g.N, scale2);
+                       (int)g.N, scale2, out);
   return check_launch("k_fwd");
 }
 
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, const void* dout, const float* lse2,
                              const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
-                             hipStream_t st) {
+                             const RowMap& out, hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   {
@@ -878,11 +897,11 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
     if (g.d == 64)
       hipLaunchKernelGGL(k_dq<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                          (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
-                         (int)g.N, scale2, sm_scale);
+                         (int)g.N, scale2, sm_scale, out);
     else
       hipLaunchKernelGGL(k_dq<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                          (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
-                         (int)g.N, scale2, sm_scale);
+                         (int)g.N, scale2, sm_scale, out);
   }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
@@ -890,11 +909,11 @@ prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cn
   if (g.d == 64)
     hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
-                       g.hpg, (int)g.N, scale2, sm_scale);
+                       g.hpg, (int)g.N, scale2, sm_scale, out);
   else
     hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
-                       g.hpg, (int)g.N, scale2, sm_scale);
+                       g.hpg, (int)g.N, scale2, sm_scale, out);
   return check_launch("k_dkdv");
 }
 

@@ -92,6 +92,41 @@ __device__ __forceinline__ int block_of_row(const int32_t* bs, int nbmax, int ro
   return lo;
 }
 
+// Token of a block-order row.  Position p (0..511) of zone m's block-order range, the zone's
+// blocks having edges (bT, bH, bW) in {2, 4, 8}: blocks in raster order over the zone's block
+// grid, tokens in raster order inside a block.  Returns n = (t*H + h)*W + w.
+__device__ __forceinline__ int ilog2_edge(int x) { return x == 2 ? 1 : x == 4 ? 2 : 3; }
+__device__ __forceinline__ int64_t zone_pos_token(int m, int p, int bT, int bH, int bW, int H, int W, int ZH,
+                                                  int ZW) {
+  const int lT = ilog2_edge(bT), lH = ilog2_edge(bH), lW = ilog2_edge(bW);
+  const int lB = lT + lH + lW, lnW = 3 - lW, lnH = 3 - lH;
+  const int beta = p >> lB, iota = p & ((1 << lB) - 1);
+  const int bw = beta & ((1 << lnW) - 1), bh = (beta >> lnW) & ((1 << lnH) - 1), bt = beta >> (lnW + lnH);
+  const int iw = iota & (bW - 1), ih = (iota >> lW) & (bH - 1), it = iota >> (lW + lH);
+  const int zt = m / (ZH * ZW), zh = (m / ZW) % ZH, zw = m % ZW;
+  return ((int64_t)(zt * 8 + (bt << lT) + it) * H + zh * 8 + (bh << lH) + ih) * W + zw * 8 + (bw << lW) + iw;
+}
+
+// Where the attention kernels put an output row: block order [heads, N, d] when shape_idx is
+// NULL, else token order [N, heads, d] (the row's token from its zone's shape).
+struct RowMap {
+  const uint8_t* shape_idx;  // [groups, Z] or NULL
+  int H, W, ZH, ZW, Z;
+};
+inline RowMap block_rows() { return RowMap{nullptr, 0, 0, 0, 0, 0}; }
+inline RowMap token_rows(const Geom& g, const uint8_t* shape_idx) {
+  return RowMap{shape_idx, g.H, g.W, g.ZH, g.ZW, g.Z};
+}
+// Row index (in rows of d elements) of block-order row `row` of head h (group grp); `shapes` is
+// the translation unit's device copy of the shape table.
+__device__ __forceinline__ int64_t out_row(const RowMap& rm, const ShapeEntry* shapes, int grp, int h, int heads,
+                                           int64_t N, int row) {
+  if (!rm.shape_idx) return (int64_t)h * N + row;
+  const int m = row >> 9;
+  const ShapeEntry se = shapes[rm.shape_idx[(int64_t)grp * rm.Z + m]];
+  return zone_pos_token(m, row & 511, se.bT, se.bH, se.bW, rm.H, rm.W, rm.ZH, rm.ZW) * heads + h;
+}
+
 // ---- stage launchers (defined in the .hip files; arguments already validated) ---------
 
 prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, float eps, float* gout,
@@ -108,14 +143,17 @@ prism_status launch_pool(const Geom& g, const int32_t* block_start, int count,
 prism_status launch_select(const Geom& g, const int32_t* block_start, const float* qbar,
                            const float* kbar, float sm_scale, int32_t k_abs, double k_frac,
                            double p, int32_t* sel_count, int32_t* sel_idx, hipStream_t st);
+// out: where o, o_lo (forward) and dq, dk, dv (backward) go; o_in: where the backward reads o,
+// o_lo.  dout and everything else stay in block order.
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
-                            const void* v, void* o, void* o_lo, float* lse, hipStream_t st);
+                            const void* v, void* o, void* o_lo, float* lse, const RowMap& out,
+                            hipStream_t st);
 size_t bsa_bwd_workspace_bytes(const Geom& g);
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
                             const void* v, const void* o, const void* o_lo, const void* dout,
                             const float* lse, float* dq, float* dk, float* dv, void* ws,
-                            hipStream_t st);
+                            const RowMap& o_in, const RowMap& out, hipStream_t st);
 
 }  // namespace prism

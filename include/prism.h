@@ -189,6 +189,32 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
                            float* dk, float* dv, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- a6 / a7 with token-order outputs ------------------------------------------------ *
+ * The same attention as prism_bsa_fwd / prism_bsa_bwd, with the caller-facing tensors in token
+ * order [N, heads, head_dim]: the kernels write each output row straight to its token (the
+ * inverse of the block order given by shape_idx, which must be the shape map the block-order
+ * q, k, v were permuted with), so the separate inverse permutes of O and of the gradients (and
+ * their block-order buffers) are not needed.  Results are bitwise those of the block-order
+ * calls followed by prism_permute(inverse = 1).
+ * prism_bsa_fwd_tok: q, k, v block order (as for prism_bsa_fwd); o and o_lo out in token order;
+ *   lse out [heads, N] in block order.
+ * prism_bsa_bwd_tok: q, k, v block order; o, o_lo (prism_bsa_fwd_tok's outputs) and dout in
+ *   token order; lse block order; dq, dk, dv out [N, heads, head_dim] fp32 in token order.
+ *   The workspace (prism_bsa_bwd_tok_workspace_bytes, 256-byte aligned) also holds a
+ *   block-order copy of dout.
+ * Errors as for the block-order calls; shape_idx must be non-NULL. */
+prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
+                               const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
+                               const void* q, const void* k, const void* v, void* o, void* o_lo,
+                               float* lse, void* stream);
+size_t prism_bsa_bwd_tok_workspace_bytes(const prism_problem* pb);
+prism_status prism_bsa_bwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
+                               const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const void* o_lo, const void* dout, const float* lse, float* dq,
+                               float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ---- measurement hook --------------------------------------------------------------- *
  * Records the HIP events start_event / stop_event (hipEvent_t passed as void*, created by
  * the caller) immediately before and after every later launch of the library kernel named

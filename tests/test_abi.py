@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert P.prism_abi_version() == 1
@@ -100,6 +100,25 @@ def test_backward_workspace(L):
     assert L.prism_bsa_bwd(*args, FAKE, need - 1, None) == 6
     assert L.prism_bsa_bwd(*args, MISALIGNED, need, None) == 5
     assert P.prism_bsa_bwd_workspace_bytes(_pb(T=3)) == 0
+
+
+def test_token_order_attention_validation(L):
+    pb = _pb()
+    fwd = L.prism_bsa_fwd_tok
+    # shape_idx is required: the output rows' tokens come from it
+    assert fwd(ctypes.byref(pb), None, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
+    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 3
+    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, MISALIGNED, None, FAKE, None) == 5
+    need = P.prism_bsa_bwd_tok_workspace_bytes(pb)
+    N, d = 8 * 16 * 16, 64
+    # the block-order workspace plus a bf16 block-order copy of dO
+    assert need >= P.prism_bsa_bwd_workspace_bytes(pb) + 2 * N * d * 2
+    args = [ctypes.byref(pb)] + [FAKE] * 4 + [0.125] + [FAKE] * 10
+    assert L.prism_bsa_bwd_tok(*args, FAKE, need - 1, None) == 6
+    assert L.prism_bsa_bwd_tok(*args, MISALIGNED, need, None) == 5
+    assert L.prism_bsa_bwd_tok(ctypes.byref(pb), None, *([FAKE] * 3), 0.125, *([FAKE] * 10), FAKE, need,
+                               None) == 1
+    assert P.prism_bsa_bwd_tok_workspace_bytes(_pb(T=3)) == 0
 
 
 def test_selection_capacity_limit(L):

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import synth
+from dynamic_block_sparse_var_amd import PrismLayer
 from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, compare_shapes, f64, say)
 
 pytestmark = pytest.mark.gpu
@@ -245,3 +246,36 @@ def test_dense_selection_through_select(run):
         n = int(nb[h // hpg])
         assert (cnt[h, :n] == n).all() and (cnt[h, n:] == 0).all()
         np.testing.assert_array_equal(idx[h, :n, :n], np.broadcast_to(np.arange(n), (n, n)))
+
+
+def test_token_order_attention_bitwise(run):
+    """prism_bsa_fwd_tok / prism_bsa_bwd_tok write O, its residual and the gradients straight
+    to token order: they must equal the block-order calls followed by the inverse permute, bit
+    for bit (same arithmetic, different output rows), given the oracle's plan and mask."""
+    c = run.cfg
+    _gpu_attention(run)
+    L = run.layer
+    ref = {"o": L.o.clone(), "lse": L.lse.clone()}
+    if run.backward:
+        ref.update(dq=L.dq.clone(), dk=L.dk.clone(), dv=L.dv.clone())
+        if L.op_lo is not None:
+            from dynamic_block_sparse_var_amd import prism_permute
+
+            lo = torch.empty_like(L.o)
+            prism_permute(run.pb, L.shape_idx, 1, [L.op_lo], [lo])
+            ref["o_lo"] = lo
+    T = PrismLayer(run.pb, backward=run.backward, token_io=True)
+    for name in ("shape_idx", "zone_block_off", "block_start", "qp", "kp", "vp", "sel_count", "sel_idx"):
+        getattr(T, name).copy_(getattr(L, name))
+    T.attend(c.sm_scale)
+    if run.backward:
+        T.backward(run.dout, c.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(T.o, ref["o"])
+    assert torch.equal(T.lse, ref["lse"])
+    if run.backward:
+        for name in ("dq", "dk", "dv"):
+            assert torch.equal(getattr(T, name), ref[name]), name
+        if "o_lo" in ref:
+            assert torch.equal(T.o_lo, ref["o_lo"])
+    say(f"  token-order outputs bitwise equal to block order + inverse permute ({c.name})")
