@@ -75,6 +75,17 @@ def candidates():
     return edges[:n].copy(), vol[:n].copy()
 
 
+def audio_norms(hhat, squared=False):
+    """RG M1 audio coupling input: per-token L2 norm of hhat [N, C] (sum of squares if squared)."""
+    lib = _load()
+    x = _f32(hhat)
+    N, C = x.shape
+    a = np.zeros(N)
+    rc = lib.orc_audio_norms(ctypes.c_int64(N), _c_int(C), _p(x), _c_int(1 if squared else 0), _p(a))
+    _check(rc, "audio_norms")
+    return a
+
+
 def zone_stats(v, a, T, H, W, heads, d, groups, eps, nthreads=None):
     """RG M1: zone statistics and the composite indicator g (see prism_oracle.h)."""
     lib = _load()

@@ -684,3 +684,18 @@ int orc_attn_bwd(int heads, int groups, int N, int d, int nbmax, const int32_t* 
   free(tr_off); free(need); free(dqneed); free(tr_list); free(fill);
   return 0;
 }
+
+/* RG M1 (audio coupling input): a_n = || hhat_n ||_2 over the channels of token n, the
+ * cross-attention output norm the zone statistics consume; sum of squares when squared != 0. */
+int orc_audio_norms(int64_t N, int channels, const float* hhat, int squared, double* a) {
+  if (N < 0 || channels <= 0 || !hhat || !a) return -1;
+  for (int64_t n = 0; n < N; ++n) {
+    double s = 0.0;
+    for (int c = 0; c < channels; ++c) {
+      const double x = (double)hhat[n * channels + c];
+      s += x * x;
+    }
+    a[n] = squared ? s : sqrt(s);
+  }
+  return 0;
+}

@@ -111,6 +111,11 @@ int orc_attn_bwd(int heads, int groups, int N, int d, int nbmax,
                  double* dq, double* dk, double* dv, double* lse, double* delta,
                  int nthreads);
 
+/* RG M1 (the audio coupling field is the L2 norm of each video token's audio-to-video
+ * cross-attention output, taken from the previous layer).  hhat [N, channels] fp32 (token
+ * order) -> a [N] = sqrt(sum_c hhat[n][c]^2), or the sum of squares itself when squared != 0. */
+int orc_audio_norms(int64_t N, int channels, const float* hhat, int squared, double* a);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,44 @@ def _built():
     oracle.build(force=False)
 
 
+# ----------------------------------------------------------------- RG M1: audio coupling input
+
+def test_audio_norms_closed_forms():
+    """The coupling field is the L2 norm of each token's cross-attention output (RG M1).
+    Integer Pythagorean tuples, placed at scattered channels, give exact integer norms; the
+    squared form is the exact integer sum of squares."""
+    C = 40
+    tuples = [((3, 4), 5), ((1, 2, 2), 3), ((2, 3, 6), 7), ((1, 4, 8), 9), ((2, 10, 11), 15),
+              ((1, 2, 4, 10), 11), ((12, 16, 21), 29)]
+    rng = np.random.default_rng(11)
+    x = np.zeros((len(tuples) + 2, C), np.float32)
+    want = np.zeros(len(tuples) + 2)
+    for i, (t, n) in enumerate(tuples):
+        ch = rng.choice(C, len(t), replace=False)
+        x[i, ch] = np.array(t) * rng.choice([-1, 1], len(t))
+        want[i] = n
+    x[-2, 17] = -6.5  # one entry: its magnitude
+    want[-2] = 6.5
+    # last row stays zero: norm 0
+    assert np.array_equal(oracle.audio_norms(x), want)
+    assert np.array_equal(oracle.audio_norms(x, squared=True), want ** 2)
+
+
+def test_audio_norms_constant_rows_and_scaling():
+    """|c| sqrt(C) for a constant row (exact when C is a perfect square); a(2^k x) = 2^k a(x)
+    exactly."""
+    for C, root in ((64, 8), (256, 16), (9, 3)):
+        c = np.array([0.75, -1.5, 3.0, -0.125], np.float32)
+        x = np.repeat(c[:, None], C, axis=1)
+        assert np.array_equal(oracle.audio_norms(x), np.abs(c).astype(np.float64) * root)
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((50, 512)).astype(np.float32)
+    a = oracle.audio_norms(x)
+    for k in (-3, 1, 5):
+        assert np.array_equal(oracle.audio_norms(x * np.float32(2.0 ** k)), a * 2.0 ** k)
+    assert (a > 0).all()
+
+
 # ----------------------------------------------------------------------------- constants
 
 
