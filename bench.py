@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 MFMA_KERNELS = ("k_fwd", "k_dq", "k_dkdv")
-HBM_KERNELS = ("k_zone_stats", "k_pool")
+HBM_KERNELS = ("k_zone_stats", "k_pool", "k_permute_pool")
 
 
 def log(*a):
@@ -243,7 +243,7 @@ def main():
     stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
               "permute_do", "bsa_bwd", "unpermute_grads"]
     if not args.block_io:
-        stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "bsa_bwd"]
+        stages = ["zone_stats", "assign_shapes", "permute_pool", "select", "bsa_fwd", "bsa_bwd"]
 
     fixed = P.fixed_shape_index((4, 4, 4)) if args.fixed_shape else None
     # dense baseline: every key block selected (k = N_b), the same kernels otherwise
@@ -263,6 +263,21 @@ def main():
             mark(1)
             P.prism_fixed_shapes(pb, fixed, L.shape_idx, L.zone_block_off, L.block_start)
         mark(2)
+        if not args.block_io:
+            # permute Q, K, V and pool Q, K in one pass; attention outputs straight to token order
+            P.prism_permute_pool(pb, L.shape_idx, L.zone_block_off, [q, k, v], [L.qp, L.kp, L.vp],
+                                 [L.qbar, L.kbar, None])
+            mark(3)
+            P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, k_abs, k_frac, cfg.p, L.sel_count,
+                                  L.sel_idx)
+            mark(4)
+            P.prism_bsa_fwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
+                                L.o_lo, L.lse)
+            mark(5)
+            P.prism_bsa_bwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
+                                L.o_lo, do, L.lse, L.dq, L.dk, L.dv, L.workspace)
+            mark(6)
+            return
         P.prism_permute(pb, L.shape_idx, 0, [q, k, v], [L.qp, L.kp, L.vp])
         mark(3)
         P.prism_pool_blocks(pb, L.block_start, [L.qp, L.kp], [L.qbar, L.kbar])
@@ -270,14 +285,6 @@ def main():
         P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, k_abs, k_frac, cfg.p, L.sel_count,
                               L.sel_idx)
         mark(5)
-        if not args.block_io:
-            P.prism_bsa_fwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
-                                L.o_lo, L.lse)
-            mark(6)
-            P.prism_bsa_bwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
-                                L.o_lo, do, L.lse, L.dq, L.dk, L.dv, L.workspace)
-            mark(7)
-            return
         P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse)
         mark(6)
         P.prism_permute(pb, L.shape_idx, 1, [L.op], [L.o])
@@ -391,12 +398,18 @@ def main():
     else:
         roof = {"kernel": dom, "bound": "mfma", "achieved": ak["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ak["mfma_frac"], "traffic": traffic.get(dom)}
-    # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
-    kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
-    kern_ms["k_permute"] = stage_ms["permute_qkv"]
+    if args.block_io:
+        # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
+        kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
+        kern_ms["k_permute"] = stage_ms["permute_qkv"]
+        hbm_names = ("k_zone_stats", "k_permute", "k_pool")
+    else:
+        # Q, K, V read and written once, pooled Q and K written
+        kbytes["k_permute_pool"] = 3 * 2 * N * H_ * d * ebytes + 2 * H_ * pb.nbmax * d * 4
+        hbm_names = ("k_zone_stats", "k_permute_pool")
     hbm = {kn: {"ms": round(kern_ms[kn], 4), "GB/s": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9, 1),
                 "frac": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-           for kn in ("k_zone_stats", "k_permute", "k_pool")}
+           for kn in hbm_names}
 
     out = {
         "metric": "2K-shaped sparse-attn fwd+bwd ms/layer, TFLOP/s and % bf16 MFMA peak",
@@ -431,6 +444,26 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    # auxiliary, not part of the step: the audio-norm producer (the next layer's coupling input)
+    # on a cross-attention output of this GPU's heads x d channels, device-generated
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    hh = torch.randn(N, H_ * d, dtype=dt, device=dev, generator=gen)
+    an = torch.empty(N, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        P.prism_audio_norms(pb, hh, an)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        P.prism_audio_norms(pb, hh, an)
+    e1.record()
+    torch.cuda.synchronize()
+    an_ms = e0.elapsed_time(e1) / 10
+    an_bytes = N * H_ * d * ebytes + 4 * N
+    out["aux_stages"] = {"audio_norms": {"ms": round(an_ms, 4), "channels": H_ * d,
+                                         "GB/s": round(an_bytes / (an_ms * 1e-3) / 1e9, 1),
+                                         "frac": round(an_bytes / (an_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    del hh, an
     if not args.no_cpu_baseline and not (args.dense or args.fixed_shape):
         log("bench: CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(inp, budget_s=args.cpu_seconds)

@@ -91,6 +91,8 @@ def lib():
         "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
+        "prism_audio_norms": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp]),
+        "prism_permute_pool": (_i32, [_PB, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
         "prism_bsa_fwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "prism_bsa_bwd_tok_workspace_bytes": (ctypes.c_size_t, [_PB]),
         "prism_bsa_bwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -142,6 +144,12 @@ def prism_shape_table() -> list[tuple[int, int, int]]:
     return [tuple(buf[3 * i:3 * i + 3]) for i in range(n)]
 
 
+def prism_audio_norms(pb, hhat, a, squared=False, stream=None):
+    """Per-token L2 norm (or sum of squares) of hhat [N, C] -> a [N] fp32."""
+    _check(lib().prism_audio_norms(ctypes.byref(pb), _p(hhat), int(hhat.shape[-1]), 1 if squared else 0, _p(a),
+                                   _stream(stream)), "prism_audio_norms")
+
+
 def prism_zone_stats(pb, v, a, eps, g, rho, zone_audio, stream=None):
     _check(lib().prism_zone_stats(ctypes.byref(pb), _p(v), _p(a), eps, _p(g), _p(rho), _p(zone_audio),
                                   _stream(stream)), "prism_zone_stats")
@@ -166,6 +174,17 @@ def prism_permute(pb, shape_idx, inverse, src, dst, stream=None):
     src, dst = list(src), list(dst)
     _check(lib().prism_permute(ctypes.byref(pb), _p(shape_idx), int(inverse), len(src), _ptr_array(src),
                                _ptr_array(dst), _stream(stream)), "prism_permute")
+
+
+def prism_permute_pool(pb, shape_idx, zone_block_off, src, dst, xbar=None, stream=None):
+    """Token -> block order for the tensors in src (into dst) and, where xbar[i] is a tensor,
+    their pooled block means (prism_permute + prism_pool_blocks in one pass)."""
+    n = len(src)
+    pooled = None
+    if xbar is not None:
+        pooled = (ctypes.c_void_p * n)(*[None if x is None else x.data_ptr() for x in xbar])
+    _check(lib().prism_permute_pool(ctypes.byref(pb), _p(shape_idx), _p(zone_block_off), n, _ptr_array(src),
+                                    _ptr_array(dst), pooled, _stream(stream)), "prism_permute_pool")
 
 
 def prism_pool_blocks(pb, block_start, x_perm, xbar, stream=None):
@@ -294,8 +313,12 @@ class PrismLayer:
 
     def select(self, q, k, v, sm_scale, k_abs, k_frac, p, stream=None):
         pb = self.pb
-        prism_permute(pb, self.shape_idx, 0, [q, k, v], [self.qp, self.kp, self.vp], stream)
-        prism_pool_blocks(pb, self.block_start, [self.qp, self.kp], [self.qbar, self.kbar], stream)
+        if self.token_io:
+            prism_permute_pool(pb, self.shape_idx, self.zone_block_off, [q, k, v], [self.qp, self.kp, self.vp],
+                               [self.qbar, self.kbar, None], stream)
+        else:
+            prism_permute(pb, self.shape_idx, 0, [q, k, v], [self.qp, self.kp, self.vp], stream)
+            prism_pool_blocks(pb, self.block_start, [self.qp, self.kp], [self.qbar, self.kbar], stream)
         prism_select_blocks(pb, self.block_start, self.qbar, self.kbar, sm_scale, k_abs, k_frac, p, self.sel_count,
                             self.sel_idx, stream)
 

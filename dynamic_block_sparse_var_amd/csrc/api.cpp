@@ -153,6 +153,19 @@ int32_t prism_shape_table(int32_t* edges) {
   return 16;
 }
 
+prism_status prism_audio_norms(const prism_problem* pb, const void* hhat, int32_t channels, int32_t squared, float* a,
+                               void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(hhat, "hhat"));
+  PRISM_TRY(need_aligned(a, "a"));
+  if (channels <= 0 || channels % 8 != 0 || channels > (1 << 20))
+    return fail(PRISM_E_RANGE, "channels = %d must be a positive multiple of 8, at most 2^20", channels);
+  if (squared != 0 && squared != 1) return fail(PRISM_E_RANGE, "squared = %d must be 0 or 1", squared);
+  Geom gm = make_geom(pb);
+  return launch_audio_norms(gm, hhat, channels, squared, a, (hipStream_t)stream);
+}
+
 prism_status prism_zone_stats(const prism_problem* pb, const void* v, const float* a, float eps, float* g,
                               float* rho, float* zone_audio, void* stream) {
   g_err[0] = 0;
@@ -214,6 +227,25 @@ prism_status prism_permute(const prism_problem* pb, const uint8_t* shape_idx, in
   }
   Geom gm = make_geom(pb);
   return launch_permute(gm, shape_idx, inverse, count, src, dst, (hipStream_t)stream);
+}
+
+prism_status prism_permute_pool(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* zone_block_off,
+                                int32_t count, const void* const* src, void* const* dst, float* const* xbar,
+                                void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(shape_idx, "shape_idx"));
+  PRISM_TRY(need_aligned(zone_block_off, "zone_block_off"));
+  if (count < 1 || count > 4) return fail(PRISM_E_RANGE, "count = %d not in [1, 4]", count);
+  PRISM_TRY(need_ptr(src, "src"));
+  PRISM_TRY(need_ptr(dst, "dst"));
+  for (int i = 0; i < count; ++i) {
+    PRISM_TRY(need_aligned(src[i], "src[i]"));
+    PRISM_TRY(need_aligned(dst[i], "dst[i]"));
+    if (xbar && xbar[i]) PRISM_TRY(need_aligned(xbar[i], "xbar[i]"));
+  }
+  Geom gm = make_geom(pb);
+  return launch_permute_pool(gm, shape_idx, zone_block_off, count, src, dst, xbar, (hipStream_t)stream);
 }
 
 prism_status prism_pool_blocks(const prism_problem* pb, const int32_t* block_start, int32_t count,

@@ -129,6 +129,8 @@ __device__ __forceinline__ int64_t out_row(const RowMap& rm, const ShapeEntry* s
 
 // ---- stage launchers (defined in the .hip files; arguments already validated) ---------
 
+prism_status launch_audio_norms(const Geom& g, const void* hhat, int channels, int squared, float* a,
+                                hipStream_t st);
 prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, float eps, float* gout,
                                float* rho, float* zone_audio, hipStream_t st);
 prism_status launch_assign_shapes(const Geom& g, const float* gin, const float* rho, float tau128,
@@ -140,6 +142,9 @@ prism_status launch_permute(const Geom& g, const uint8_t* shape_idx, int inverse
                             const void* const* src, void* const* dst, hipStream_t st);
 prism_status launch_pool(const Geom& g, const int32_t* block_start, int count,
                          const void* const* x, float* const* xbar, hipStream_t st);
+prism_status launch_permute_pool(const Geom& g, const uint8_t* shape_idx, const int32_t* zone_block_off,
+                                 int count, const void* const* src, void* const* dst, float* const* xbar,
+                                 hipStream_t st);
 prism_status launch_select(const Geom& g, const int32_t* block_start, const float* qbar,
                            const float* kbar, float sm_scale, int32_t k_abs, double k_frac,
                            double p, int32_t* sel_count, int32_t* sel_idx, hipStream_t st);

@@ -11,6 +11,9 @@
 // g = r + abar * vhat + eps.
 // k_assign_shapes: one workgroup per head group: volume, l*, nearest candidate, exclusive
 // scan of blocks per zone, block start rows.
+// k_audio_norms: the coupling field the statistics read, a_n = || hhat_n ||_2 of each token's
+// cross-attention output: one wave per token row at a time, 16-byte loads, fp32 sums of
+// squares per lane, a fixed-order butterfly across the wave.
 #include <math.h>
 
 #include "prism_internal.h"
@@ -274,7 +277,50 @@ __global__ __launch_bounds__(256) void k_fixed_shapes(int shape_index, uint8_t* 
   for (int j = Z * nb + blockIdx.x * 256 + threadIdx.x; j <= nbmax; j += gridDim.x * 256) bs[j] = N;
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_audio_norms(const uint4* __restrict__ x, int64_t N, int chunks, int squared,
+                                                     float* __restrict__ a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; n < N; n += nwaves) {
+    const uint4* row = x + n * chunks;
+    float s = 0.f;
+    for (int c = lane; c < chunks; c += 64) {
+      const uint4 u = row[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+          const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+          s = fmaf(lo, lo, s);
+          s = fmaf(hi, hi, s);
+        } else {
+          const float f = __uint_as_float(w[i]);
+          s = fmaf(f, f, s);
+        }
+      }
+    }
+    s = wave_sum(s);
+    if (lane == 0) a[n] = squared ? s : sqrtf(s);
+  }
+}
+
 }  // namespace
+
+prism_status launch_audio_norms(const Geom& g, const void* hhat, int channels, int squared, float* a,
+                                hipStream_t st) {
+  const int chunks = channels * g.esize / 16;
+  const int64_t wgs = (g.N + 3) / 4;
+  const unsigned grid = (unsigned)(wgs < 8192 ? wgs : 8192);
+  KernelTrace tr("k_audio_norms", st);
+  if (g.bf16)
+    hipLaunchKernelGGL(k_audio_norms<true>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(hhat), g.N,
+                       chunks, squared, a);
+  else
+    hipLaunchKernelGGL(k_audio_norms<false>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(hhat), g.N,
+                       chunks, squared, a);
+  return check_launch("k_audio_norms");
+}
 
 prism_status launch_zone_stats(const Geom& g, const void* v, const float* a, float eps, float* gout, float* rho,
                                float* zone_audio, hipStream_t st) {

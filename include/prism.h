@@ -72,6 +72,16 @@ const char* prism_last_error(void);
  * Writes 48 int32 into the HOST array edges ([16][3]); returns 16. */
 int32_t prism_shape_table(int32_t* edges);
 
+/* ---- a1 input: the audio coupling field (RG M1) ------------------------------------- *
+ * The statistics read, per video token, the L2 norm of that token's audio-to-video
+ * cross-attention output, cached from the preceding layer: a[n] = sqrt(sum_c hhat[n][c]^2)
+ * with fp32 accumulation (squared = 1: the sum of squares itself, for a caller whose hhat is
+ * split over channels across devices and adds the partial sums before the root).
+ * hhat: [N, channels] dtype, token order; channels a positive multiple of 8 (at most 2^20).
+ * a:    out [N] fp32, the `a` argument of prism_zone_stats. */
+prism_status prism_audio_norms(const prism_problem* pb, const void* hhat, int32_t channels,
+                               int32_t squared, float* a, void* stream);
+
 /* ---- a1: zone statistics (RG M1) ---------------------------------------------------- *
  * For each head group g and zone m, over the group's D = (heads/groups)*head_dim channels:
  *   sigma^2_{v,d}(m) = (1/D) sum_c (1/8) sum_i (Vbar^{(d)}_{m,i,c} - mu_{m,c})^2, where
@@ -135,6 +145,18 @@ prism_status prism_permute(const prism_problem* pb, const uint8_t* shape_idx, in
  * [heads, NBMAX, head_dim] fp32 outputs. */
 prism_status prism_pool_blocks(const prism_problem* pb, const int32_t* block_start, int32_t count,
                                const void* const* x_perm, float* const* xbar, void* stream);
+
+/* ---- a3 + a4 in one pass ------------------------------------------------------------ *
+ * Token -> block order for count (1..4) tensors, as prism_permute(inverse = 0), and for every
+ * tensor i with xbar[i] != NULL also its pooled block means, as prism_pool_blocks on dst[i]
+ * (bitwise the same values, rows j >= N_b zero), without reading the permuted tensor again.
+ * src, dst, xbar: HOST arrays of count device pointers; xbar itself may be NULL (no pooling).
+ * zone_block_off: [groups, Z+1] from prism_assign_shapes / prism_fixed_shapes for the same
+ * shape_idx. */
+prism_status prism_permute_pool(const prism_problem* pb, const uint8_t* shape_idx,
+                                const int32_t* zone_block_off, int32_t count,
+                                const void* const* src, void* const* dst, float* const* xbar,
+                                void* stream);
 
 /* ---- a5: hybrid Top-k / Top-p block selection (RG M3 attended-set equation) ---------- *
  * Per head h and query block i < N_b: s_ij = sm_scale * qbar_i . kbar_j (fp32), P_i = softmax

@@ -18,6 +18,9 @@ f, phi, noise_Q, noise_K, noise_V, audio centres, audio noise, dO (PCG64 each).
 * bf16 configs are rounded once, round-to-nearest-even, on the host; the arrays returned
   here hold exactly the rounded values (as float32), so both sides see the same numbers.
 * Attention scale sm_scale = gamma / sqrt(d).
+* Cross-attention output hhat [N, C] for the audio-norm producer (make_hhat): the ninth
+  child of the same seed sequence draws signs s[n, c] in {-1, +1}; hhat[n, c] =
+  a[n] * s[n, c] / sqrt(C), a field whose rows have the audio norms a by construction.
 """
 from __future__ import annotations
 
@@ -156,3 +159,12 @@ def make_inputs(cfg: Config, with_dout: bool | None = None) -> dict:
 
     return dict(cfg=cfg, q=q, k=k, v=v, a=a, dout=dout, sm_scale=cfg.sm_scale, k_abs=cfg.k_abs,
                 k_frac=cfg.k_frac, p=cfg.p, tau128=cfg.tau128, tau256=cfg.tau256, eps=cfg.eps)
+
+
+def make_hhat(cfg: Config, a: np.ndarray, channels: int) -> np.ndarray:
+    """Cross-attention output rows [N, channels] built to have the per-token norms a (random
+    signs times a / sqrt(channels)); float32, rounded to bf16 for bf16 configs."""
+    rng = np.random.default_rng(np.random.SeedSequence(cfg.seed).spawn(9)[8])
+    s = rng.integers(0, 2, size=(a.shape[0], channels)).astype(np.float32) * 2.0 - 1.0
+    x = (s * (a.astype(np.float64)[:, None] / math.sqrt(channels))).astype(np.float32)
+    return _round_bf16(x) if cfg.dtype == "bf16" else x

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert P.prism_abi_version() == 1
@@ -81,6 +81,11 @@ def test_scalar_ranges_rejected(L):
     assert L.prism_permute(ctypes.byref(pb), FAKE, 2, 1, arr, arr, None) == 3
     assert L.prism_permute(ctypes.byref(pb), FAKE, 0, 5, arr, arr, None) == 3
     assert L.prism_pool_blocks(ctypes.byref(pb), FAKE, 0, arr, arr, None) == 3
+    assert L.prism_permute_pool(ctypes.byref(pb), FAKE, FAKE, 0, arr, arr, None, None) == 3
+    assert L.prism_permute_pool(ctypes.byref(pb), FAKE, FAKE, 5, arr, arr, arr, None) == 3
+    bad = (ctypes.c_void_p * 2)(0x10000, 0x10008)
+    assert L.prism_permute_pool(ctypes.byref(pb), FAKE, FAKE, 2, arr, arr, bad, None) == 5
+    assert L.prism_permute_pool(ctypes.byref(pb), None, FAKE, 1, arr, arr, None, None) == 1
     assert L.prism_fixed_shapes(ctypes.byref(pb), 16, FAKE, FAKE, FAKE, None) == 3
     assert L.prism_fixed_shapes(ctypes.byref(pb), -1, FAKE, FAKE, FAKE, None) == 3
 
@@ -100,6 +105,16 @@ def test_backward_workspace(L):
     assert L.prism_bsa_bwd(*args, FAKE, need - 1, None) == 6
     assert L.prism_bsa_bwd(*args, MISALIGNED, need, None) == 5
     assert P.prism_bsa_bwd_workspace_bytes(_pb(T=3)) == 0
+
+
+def test_audio_norms_validation(L):
+    pb = _pb()
+    assert L.prism_audio_norms(ctypes.byref(pb), FAKE, 0, 0, FAKE, None) == 3
+    assert L.prism_audio_norms(ctypes.byref(pb), FAKE, 12, 0, FAKE, None) == 3
+    assert L.prism_audio_norms(ctypes.byref(pb), FAKE, 64, 2, FAKE, None) == 3
+    assert L.prism_audio_norms(ctypes.byref(pb), None, 64, 0, FAKE, None) == 1
+    assert L.prism_audio_norms(ctypes.byref(pb), FAKE, 64, 0, MISALIGNED, None) == 5
+    assert L.prism_audio_norms(ctypes.byref(_pb(T=3)), FAKE, 64, 0, FAKE, None) == 2
 
 
 def test_token_order_attention_validation(L):

@@ -279,3 +279,20 @@ def test_token_order_attention_bitwise(run):
         if "o_lo" in ref:
             assert torch.equal(T.o_lo, ref["o_lo"])
     say(f"  token-order outputs bitwise equal to block order + inverse permute ({c.name})")
+
+
+def test_permute_pool_bitwise(run):
+    """prism_permute_pool = prism_permute + prism_pool_blocks, bit for bit, with pooled rows past
+    N_b zero (the outputs are pre-filled with NaN) and no pooling for a tensor whose xbar is
+    None."""
+    from dynamic_block_sparse_var_amd import prism_permute, prism_permute_pool, prism_pool_blocks
+
+    run.inject_oracle_plan()
+    L = run.layer
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    prism_pool_blocks(run.pb, L.block_start, [L.qp, L.kp], [L.qbar, L.kbar])
+    outs = [torch.full_like(t, float("nan")) for t in (L.qp, L.kp, L.vp, L.qbar, L.kbar)]
+    prism_permute_pool(run.pb, L.shape_idx, L.zone_block_off, [run.q, run.k, run.v], outs[:3], outs[3:] + [None])
+    torch.cuda.synchronize()
+    for mine, ref in zip(outs, (L.qp, L.kp, L.vp, L.qbar, L.kbar)):
+        assert torch.equal(mine, ref)
