@@ -132,3 +132,33 @@ def test_attention_full_sampled(run):
             dk_scale = L.dkp[h].double().abs().sum(0).max().item()
             say(f"  head {h}: |sum dV - sum dO| rel {rel:.2e}; |sum dK| / sum |dK| {dk_sum / dk_scale:.2e}")
             assert rel < 1e-4 and dk_sum <= 1e-4 * dk_scale
+
+
+def test_token_order_path_full(run):
+    """The path the benchmark times (one-pass permute+pool, token-order attention) at full size:
+    bitwise equal to the block-order calls plus permutes, whose parity the tests above check,
+    given the oracle's plan and mask."""
+    from dynamic_block_sparse_var_amd import PrismLayer, prism_permute, prism_permute_pool
+
+    c = run.cfg
+    run.inject_oracle_plan()
+    L = run.layer
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    run.inject_oracle_mask()
+    L.attend(c.sm_scale)
+    if run.backward:
+        L.backward(run.dout, c.sm_scale)
+    T = PrismLayer(run.pb, backward=run.backward, token_io=True)
+    for name in ("shape_idx", "zone_block_off", "block_start", "sel_count", "sel_idx"):
+        getattr(T, name).copy_(getattr(L, name))
+    prism_permute_pool(run.pb, T.shape_idx, T.zone_block_off, [run.q, run.k, run.v], [T.qp, T.kp, T.vp],
+                       [T.qbar, T.kbar, None])
+    T.attend(c.sm_scale)
+    if run.backward:
+        T.backward(run.dout, c.sm_scale)
+    torch.cuda.synchronize()
+    for name in ("qp", "kp", "vp", "o", "lse") + (("dq", "dk", "dv") if run.backward else ()):
+        assert torch.equal(getattr(T, name), getattr(L, name)), name
+    say(f"  {c.name}: token-order path bitwise equal to block order + permutes")
+    del T
+    torch.cuda.empty_cache()
