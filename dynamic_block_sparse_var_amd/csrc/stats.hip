@@ -2,8 +2,8 @@
 //
 // k_zone_stats: one workgroup per (zone, head group).  Each thread owns channel pairs of the
 // group and walks the zone's 512 tokens in raster order with 4-byte (bf16x2) or 8-byte
-// (fp32x2) loads, so each wavefront reads 256-512 contiguous bytes of a token row per load.
-// Per channel it keeps the 8 H-slice and 8 W-slice sums in registers and folds each T slice
+// (fp32x2) loads, so each wavefront reads 256-512 contiguous bytes of a token row per load;
+// the 64 loads of a T slice are issued together (64 in flight per wave).  Per channel it keeps the 8 H-slice and 8 W-slice sums in registers and folds each T slice
 // into a sum of squares as soon as it is complete; values are shifted by the zone's first
 // token so the variance formulas do not cancel.  Partial variances are reduced over the
 // workgroup in a fixed order (deterministic).
@@ -32,6 +32,33 @@ __device__ __forceinline__ float2 load_pair(const void* base, int64_t elem) {
   }
 }
 
+// raw element pairs as loaded (bf16x2 in one dword, or two floats), converted after the loads of
+// a whole T slice have been issued
+template <bool BF16>
+struct RawPair {
+  using type = float2;
+};
+template <>
+struct RawPair<true> {
+  using type = uint32_t;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename RawPair<BF16>::type load_raw(const void* base, int64_t elem) {
+  if constexpr (BF16)
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(base) + elem);
+  else
+    return *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(base) + elem);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float2 raw_pair(typename RawPair<BF16>::type u) {
+  if constexpr (BF16)
+    return make_float2(bf16_lo(u), bf16_hi(u));
+  else
+    return u;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_zone_stats(const void* __restrict__ v, const float* __restrict__ a,
                                                     float* __restrict__ gout, float* __restrict__ rho,
@@ -56,14 +83,21 @@ __global__ __launch_bounds__(256) void k_zone_stats(const void* __restrict__ v, 
     const int64_t n00 = ((int64_t)(zt * 8) * H + zh * 8) * W + zw * 8;
     const float2 shift = load_pair<BF16>(v, n00 * rowlen + c0);
     for (int lt = 0; lt < 8; ++lt) {
+      // the slice's 64 loads are all issued before any is used, so a wave keeps 64 of them in
+      // flight instead of waiting for each
+      typename RawPair<BF16>::type raw[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const int64_t nrow = ((int64_t)(zt * 8 + lt) * H + zh * 8 + (i >> 3)) * W + zw * 8;
+        raw[i] = load_raw<BF16>(v, (nrow + (i & 7)) * rowlen + c0);
+      }
       float ts0 = 0.f, ts1 = 0.f;
 #pragma unroll
       for (int lh = 0; lh < 8; ++lh) {
-        const int64_t nrow = ((int64_t)(zt * 8 + lt) * H + zh * 8 + lh) * W + zw * 8;
         float r0 = 0.f, r1 = 0.f;
 #pragma unroll
         for (int lw = 0; lw < 8; ++lw) {
-          float2 x = load_pair<BF16>(v, (nrow + lw) * rowlen + c0);
+          const float2 x = raw_pair<BF16>(raw[8 * lh + lw]);
           const float y0 = x.x - shift.x, y1 = x.y - shift.y;
           Ws0[lw] += y0;
           Ws1[lw] += y1;
