@@ -449,8 +449,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
         oacc[db] = mfma(vt[db], p_lo, oacc[db]);
       }
     };
+    // the PV products are issued at raised wave priority, so that the other workgroup's wave on
+    // the SIMD, in its softmax or S phase, yields issue slots to them (measured: -1.5 %)
+    __builtin_amdgcn_s_setprio(1);
     pv(std::integral_constant<int, 0>{});
     pv(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_s_setprio(0);
   };
   if (it.valid()) {
     uint32_t soff = 0;
@@ -778,6 +782,8 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
     // dV += P^T dO, then dK += dS^T Q (P and dS as bf16 head + residual); the phases are kept
     // apart so that only one split operand set is live at a time
     __builtin_amdgcn_sched_barrier(0);
+    // the dV and dK products run at raised wave priority (as the forward's PV; measured: -1.5 %)
+    __builtin_amdgcn_s_setprio(1);
     auto pdo = [&](auto tc) __attribute__((always_inline)) {
       constexpr int t = decltype(tc)::value;
       bf16x8 pa_hi, pa_lo, dot[2];
@@ -815,6 +821,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
     };
     dsq(std::integral_constant<int, 0>{});
     dsq(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_s_setprio(0);
   };
   if (it.valid()) {
     uint32_t soff = 0;
