@@ -3,10 +3,11 @@
 // k_zone_stats: one workgroup per (zone, head group).  Each thread owns channel pairs of the
 // group and walks the zone's 512 tokens in raster order with 4-byte (bf16x2) or 8-byte
 // (fp32x2) loads, so each wavefront reads 256-512 contiguous bytes of a token row per load;
-// the 64 loads of a T slice are issued together (64 in flight per wave).  Per channel it keeps the 8 H-slice and 8 W-slice sums in registers and folds each T slice
-// into a sum of squares as soon as it is complete; values are shifted by the zone's first
-// token so the variance formulas do not cancel.  Partial variances are reduced over the
-// workgroup in a fixed order (deterministic).
+// the 64 loads of a T slice are issued together (64 in flight per wave).  Per channel it keeps
+// the 8 H-slice and 8 W-slice sums in registers and folds each T slice into a sum of squares as
+// soon as it is complete; values are shifted by the zone's first token so the variance formulas
+// do not cancel.  Partial variances are reduced over the workgroup in a fixed order
+// (deterministic).
 // k_zone_finish: one workgroup; global max of the audio zone means, then
 // g = r + abar * vhat + eps.
 // k_assign_shapes: one workgroup per head group: volume, l*, nearest candidate, exclusive
