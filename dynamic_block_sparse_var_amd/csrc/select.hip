@@ -1,8 +1,8 @@
 // select.hip -- hybrid Top-k / Top-p key-block selection (RG M3 attended-set equation).
 //
 // k_scores: per head, the fp32 block-score matrix s_ij = sm_scale * qbar_i . kbar_j as a tiled
-// GEMM (64 x 64 output tiles, 16-deep LDS slabs, 4 x 4 outputs per thread, sequential fp32
-// FMA over the head dimension).  The matrix is written into the caller's sel_idx array (same
+// GEMM (128 x 128 output tiles, 16-deep LDS slabs, 8 x 8 outputs per thread read as float4
+// rows, sequential fp32 FMA over the head dimension).  The matrix is written into the caller's sel_idx array (same
 // [heads, NBMAX, NBMAX] 4-byte footprint), row by row.
 // k_select: one 256-thread workgroup per (query block, head).  Thread t holds the row's entries
 // j = t + 256q (q < 32) as order-preserving 32-bit score keys and their exp(s - s_max).  The
@@ -26,48 +26,63 @@ constexpr int kSelMaxKeys = 8192;  // LDS sort capacity (64 KB of 64-bit keys)
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 float* __restrict__ out, const int32_t* __restrict__ block_start,
                                                 int nbmax, int hpg, int d, int N, float sm_scale) {
-  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, h = blockIdx.z;
+  constexpr int TS = 128, LD = TS + 4;  // output tile edge; LDS row stride (floats)
+  const int j0 = blockIdx.x * TS, i0 = blockIdx.y * TS, h = blockIdx.z;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   if (bs[i0] >= N || bs[j0] >= N) return;  // tile entirely past the group's blocks
-  __shared__ float As[16][68], Bs[16][68];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4];
+  __shared__ __attribute__((aligned(16))) float As[16][LD], Bs[16][LD];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  // thread (tx, ty) owns rows i0 + 8ty.. and columns j0 + 8tx.. of the tile
+  float acc[8][8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 8; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
   const float* qh = qbar + (int64_t)h * nbmax * d;
   const float* kh = kbar + (int64_t)h * nbmax * d;
-  const int lrow = threadIdx.x >> 2, le = (threadIdx.x & 3) * 4;
   for (int e0 = 0; e0 < d; e0 += 16) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + lrow < nbmax) a = *reinterpret_cast<const float4*>(qh + (int64_t)(i0 + lrow) * d + e0 + le);
-    if (j0 + lrow < nbmax) b = *reinterpret_cast<const float4*>(kh + (int64_t)(j0 + lrow) * d + e0 + le);
-    As[le + 0][lrow] = a.x; As[le + 1][lrow] = a.y; As[le + 2][lrow] = a.z; As[le + 3][lrow] = a.w;
-    Bs[le + 0][lrow] = b.x; Bs[le + 1][lrow] = b.y; Bs[le + 2][lrow] = b.z; Bs[le + 3][lrow] = b.w;
+    // the slab: 128 rows x 16 values of qbar and of kbar, stored transposed ([e][row])
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, row = idx >> 2, le = (idx & 3) * 4;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + row < nbmax) a = *reinterpret_cast<const float4*>(qh + (int64_t)(i0 + row) * d + e0 + le);
+      if (j0 + row < nbmax) b = *reinterpret_cast<const float4*>(kh + (int64_t)(j0 + row) * d + e0 + le);
+      As[le + 0][row] = a.x; As[le + 1][row] = a.y; As[le + 2][row] = a.z; As[le + 3][row] = a.w;
+      Bs[le + 0][row] = b.x; Bs[le + 1][row] = b.y; Bs[le + 2][row] = b.z; Bs[le + 3][row] = b.w;
+    }
     __syncthreads();
+    // each output accumulates over the head dimension in order, one fma per element
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float av[4], bv[4];
+      const float4 a0 = *reinterpret_cast<const float4*>(&As[e][8 * ty]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&As[e][8 * ty + 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&Bs[e][8 * tx]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&Bs[e][8 * tx + 4]);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = As[e][ty + 16 * r];
+      for (int r = 0; r < 8; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[e][tx + 16 * c];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+        for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
     }
     __syncthreads();
   }
+  const int jc = j0 + 8 * tx;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + ty + 16 * r;
+  for (int r = 0; r < 8; ++r) {
+    const int i = i0 + 8 * ty + r;
     if (i >= nbmax) continue;
+    float* o = out + ((int64_t)h * nbmax + i) * nbmax + jc;
+    if (jc + 8 <= nbmax) {
+      *reinterpret_cast<float4*>(o) =
+          make_float4(sm_scale * acc[r][0], sm_scale * acc[r][1], sm_scale * acc[r][2], sm_scale * acc[r][3]);
+      *reinterpret_cast<float4*>(o + 4) =
+          make_float4(sm_scale * acc[r][4], sm_scale * acc[r][5], sm_scale * acc[r][6], sm_scale * acc[r][7]);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tx + 16 * c;
-      if (j < nbmax) out[((int64_t)h * nbmax + i) * nbmax + j] = sm_scale * acc[r][c];
+      for (int c = 0; c < 8; ++c)
+        if (jc + c < nbmax) o[c] = sm_scale * acc[r][c];
     }
   }
 }
@@ -276,7 +291,7 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
                            int32_t* sel_idx, hipStream_t st) {
   if (g.nbmax > kSelMaxKeys)
     return fail(PRISM_E_SHAPE, "%d blocks exceed the selection capacity of %d", g.nbmax, kSelMaxKeys);
-  const int tiles = (g.nbmax + 63) / 64;
+  const int tiles = (g.nbmax + 127) / 128;
   {
   KernelTrace tr("k_scores", st);
   hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, g.heads), dim3(256), 0, st, qbar, kbar,
