@@ -253,18 +253,17 @@ __device__ __forceinline__ void tr_ops(const uint32_t (&a)[2], bf16x8 (&op)[2]) 
 // lane (vector loads), and take the current block's bounds from its lane with v_readlane, so
 // walking a list costs no dependent memory round trip per block.
 
-// Walks the 64-row tiles of the key blocks in a selection list (wave-uniform state).
+// Walks the 64-row tiles of the key blocks in a selection list (wave-uniform state).  The
+// bounds of the next batch of 64 blocks, and the list entries of the batch after it, are
+// loaded a batch ahead, so moving to a new batch waits for nothing.
 struct ListTiles {
   const int32_t* list;
   const int32_t* bs;
   int cnt, base, k, kt, kend;
-  int s_l, e_l;  // per lane: bounds of block list[base + lane]
-  __device__ void fetch(int lane) {
-    const int i = base + lane;
-    const int j = (i < cnt) ? list[i] : 0;
-    s_l = bs[j];
-    e_l = bs[j + 1];
-  }
+  int s_l, e_l;    // per lane: bounds of block list[base + lane]
+  int ps_l, pe_l;  // per lane: bounds of block list[base + 64 + lane]
+  int j_l;         // per lane: list[base + 128 + lane]
+  __device__ int entry(int i) const { return (i < cnt) ? list[i] : 0; }
   __device__ void take() {
     kt = __builtin_amdgcn_readlane(s_l, k);
     kend = __builtin_amdgcn_readlane(e_l, k);
@@ -276,7 +275,12 @@ struct ListTiles {
     base = k = 0;
     kt = kend = 0;
     if (cnt > 0) {
-      fetch(lane);
+      const int j0 = entry(lane), j1 = entry(64 + lane);
+      s_l = bs[j0];
+      e_l = bs[j0 + 1];
+      ps_l = bs[j1];
+      pe_l = bs[j1 + 1];
+      j_l = entry(128 + lane);
       take();
     }
   }
@@ -287,7 +291,15 @@ struct ListTiles {
       if (++k == 64) {
         base += 64;
         k = 0;
-        if (base < cnt) fetch(lane);
+        if (base < cnt) {
+          s_l = ps_l;
+          e_l = pe_l;
+          if (base + 64 < cnt) {
+            ps_l = bs[j_l];
+            pe_l = bs[j_l + 1];
+            if (base + 128 < cnt) j_l = entry(base + 128 + lane);
+          }
+        }
       }
       if (base + k < cnt) take();
     }
