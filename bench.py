@@ -84,6 +84,62 @@ def selection_stats(layer, pb):
     return pairs, sum(frac) / len(frac), hist, nblocks
 
 
+def forward_pair_tiles(layer, pb):
+    """(pair, union tile) units of the forward, which runs one workgroup per pair of atoms of a
+    zone and loads each tile of the union of the two lists once.  Pairs as the kernel forms them:
+    in a zone of 128- or 256-row blocks, neighbouring atoms of one block (one shared list); in a
+    zone of eight 64-row blocks, greedy matching by the number of blocks two lists share (largest
+    first, the lexicographically first pair among equal counts).  Also returns the per-atom count
+    (every atom loading its own tiles) for comparison."""
+    import numpy as np
+    import torch
+
+    N = pb.N
+    hpg = pb.heads // pb.groups
+    union_units = 0
+    atom_units = 0
+    for h in range(pb.heads):
+        bs = layer.block_start[h // hpg].long()
+        nb = int((bs[:-1] < N).sum())
+        sizes = bs[1:nb + 1] - bs[:nb]
+        tiles = (sizes // 64).float()
+        cnt = layer.sel_count[h, :nb].long()
+        M = torch.zeros(nb, nb, dtype=torch.float32, device=bs.device)
+        for r0 in range(0, nb, 1024):
+            r1 = min(nb, r0 + 1024)
+            idx = layer.sel_idx[h, r0:r1, :nb].long()
+            valid = torch.arange(nb, device=bs.device)[None, :] < cnt[r0:r1, None]
+            rows = torch.arange(r0, r1, device=bs.device)[:, None].expand_as(idx)
+            M[rows[valid], idx[valid]] = 1.0
+        ltiles = (M @ tiles).double()          # tiles in each query block's list
+        atom_units += int(((sizes // 64).double() * ltiles).sum())
+        j0 = torch.searchsorted(bs[:nb].contiguous(), torch.arange(0, N, 512, device=bs.device))
+        small = sizes[j0] == 64
+        # zones of 128/256-row blocks: B/128 pairs per block, each loading the block's list once
+        big = sizes >= 128
+        union_units += int(((sizes[big] // 128).double() * ltiles[big]).sum())
+        zs = j0[small]
+        if zs.numel() == 0:
+            continue
+        ids = zs[:, None] + torch.arange(8, device=bs.device)[None, :]
+        M8 = M[ids]                                                   # [zones, 8, nb]
+        M8t = M8.transpose(1, 2).contiguous()
+        shared = torch.bmm(M8, M8t).cpu().numpy()                     # blocks both lists hold
+        shared_t = torch.bmm(M8 * tiles[None, None, :], M8t).cpu().numpy()  # tiles both lists hold
+        lt = ltiles[ids].cpu().numpy()
+        for z in range(ids.shape[0]):
+            used = 0
+            for _ in range(4):
+                best, ba, bc = -1.0, 0, 1
+                for a in range(8):
+                    for c in range(a + 1, 8):
+                        if not (used >> a) & 1 and not (used >> c) & 1 and shared[z, a, c] > best:
+                            best, ba, bc = shared[z, a, c], a, c
+                used |= (1 << ba) | (1 << bc)
+                union_units += int(round(lt[z, ba] + lt[z, bc] - shared_t[z, ba, bc]))
+    return union_units, atom_units
+
+
 def cpu_baseline(inp, budget_s=20.0):
     """The oracle as it stands, on the same inputs: the planning half (stats, shapes, block
     layout, permute + pool of Q and K, full selection) timed in full, and the attention on a
@@ -355,14 +411,16 @@ def main():
     # Memory side of the attention kernels: the selected-tile stream this dataflow gathers.  For
     # every (64-row atom, 64-row tile of a block the atom attends to) unit it reads the two bf16
     # tiles of the other side (K and V; for dK/dV: Q and dO plus their lse2/delta rows), and
-    # each atom's own rows are read or written once.  A kernel's roofline bound is the side its
-    # arithmetic intensity (algorithmic FLOPs per tile-stream byte) falls on, against the ridge
-    # point peak FLOP/s / peak byte/s.
+    # each atom's own rows are read or written once.  The forward runs per pair of atoms and
+    # loads each tile of the union of the pair's lists once: (pair, union tile) units.  A
+    # kernel's roofline bound is the side its arithmetic intensity (algorithmic FLOPs per
+    # tile-stream byte) falls on, against the ridge point peak FLOP/s / peak byte/s.
     units = pairs // 4096
+    fwd_units, atom_units = forward_pair_tiles(L, pb)
     atoms = H_ * (N // 64)
     tile = 2 * 64 * d * ebytes
     kalg = {
-        "k_fwd": units * tile + atoms * (3 * 64 * d * ebytes + 64 * 4),
+        "k_fwd": fwd_units * tile + atoms * (3 * 64 * d * ebytes + 64 * 4),
         "k_dq": units * tile + atoms * (2 * 64 * d * ebytes + 64 * d * 4 + 2 * 64 * 4),
         "k_dkdv": units * (tile + 2 * 64 * 4) + atoms * (2 * 64 * d * ebytes + 2 * 64 * d * 4),
     }
@@ -390,6 +448,8 @@ def main():
                       "flop_per_byte": round(ai, 1),
                       "bound": "hbm" if ai < ridge else "mfma",
                       "measured_traffic_GB": round(traffic[kn] / 1e9, 2) if kn in traffic else None}
+    # the forward's stream if every atom loaded its own tiles (the dQ walk), for comparison
+    attn_k["k_fwd"]["per_atom_stream_GB"] = round((atom_units * tile + (kalg["k_fwd"] - fwd_units * tile)) / 1e9, 2)
     dom = max(MFMA_KERNELS, key=lambda kn: kern_ms[kn])
     ak = attn_k[dom]
     if ak["bound"] == "hbm":

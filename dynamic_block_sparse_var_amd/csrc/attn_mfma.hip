@@ -2,15 +2,17 @@
 // (RG M3: online-softmax attention solely across the selected key blocks S_i).
 //
 // Work decomposition.  Every block holds 64, 128 or 256 rows and starts on a multiple of 64,
-// so the unit of work is a 64-row "atom" of one head, one workgroup of four wave64s per atom.
-// The other operand is streamed in 64-row tiles (the selected key blocks of a query atom, or
-// the query blocks that selected a key atom), double-buffered in LDS: the direct global->LDS
-// loads of tile i+1 are in flight while tile i is computed, one barrier per tile.  Within a
-// tile, wave w takes 32 of the atom's rows (forward, dQ: query rows 32*(w&1)..; dK/dV: keys
-// 32*(w&1)..) against 32 of the tile's rows (32*(w>>1)..), and the two waves that share the
-// atom rows combine their partial results once at the end.  Atoms are assigned so that each
-// of the 8 XCDs walks a contiguous range of atoms (neighbouring blocks tend to select the same
-// key blocks, which may then still be in that XCD's L2).
+// so the unit of work is a 64-row "atom" of one head: one workgroup of four wave64s per atom
+// (dQ, dK/dV) or per pair of atoms of one zone (forward; the pair walks the union of its two
+// lists, so a tile both selected is loaded once).  The other operand is streamed in 64-row
+// tiles (the selected key blocks of a query atom, or the query blocks that selected a key
+// atom), double-buffered in LDS: the direct global->LDS loads of tile i+1 are in flight while
+// tile i is computed, one barrier per tile.  Within a tile, wave w takes 32 of the atom's rows
+// (forward, dQ: query rows 32*(w&1)..; dK/dV: keys 32*(w&1)..) against 32 of the tile's rows
+// (32*(w>>1)..), and the two waves that share the atom rows combine their partial results once
+// at the end.  Atoms are assigned so that each of the 8 XCDs walks a contiguous range of atoms
+// (neighbouring blocks tend to select the same key blocks, which may then still be in that
+// XCD's L2).
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16): operand A holds A[m = lane%32][8 k-values],
 // operand B holds B[8 k-values][n = lane%32]; both use lane/32 to pick which half of the 16
@@ -25,7 +27,7 @@
 //    two ds_read_b64_tr_b16 (gfx950 transposing LDS read: within each 16-lane group, lane i
 //    receives element i%4 of the 8-byte reads of lanes 4e + i/4, e = 0..3).
 //
-// Forward:  S^T = K Q^T (A = K tile, B = Q rows in registers), online softmax per query row
+// Forward:  S^T = K Q^T (A = K tile, B = Q rows in registers or LDS), online softmax per query row
 //           (a lane owns one row for 16 of the wave's 32 keys, lane ^ 32 the other 16; the
 //           running max is only raised when a tile exceeds it by 2^16, so the O rescale is
 //           rare), O^T += V^T P^T with P split into a bf16 head and residual.
@@ -34,6 +36,7 @@
 //           selection bitmap), S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q.
 // Products with P and dS use a bf16 head plus a bf16 residual of the fp32 value, so the
 // results keep fp32-level accuracy.
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -367,10 +370,161 @@ struct MaskTiles {
 // ------------------------------------------------------------------------------------------
 // forward
 
-// Workgroup = 4 waves on one 64-row atom.  Wave w owns query rows 32*(w&1).. of the atom and,
-// of every staged 64-key tile, keys 32*(w>>1)..; the two waves sharing a row half keep separate
-// online-softmax states that are merged once at the end.  Tiles are double-buffered: the loads
-// of tile i+1 are in flight while tile i is computed, with one barrier per tile.
+// Walks the union of two selection lists (those of the two query atoms of a pair): the 64-row
+// tiles of every key block in either list, in ascending order, each with the mask of the lists
+// that hold it (bit 0: first, bit 1: second).  Both lists are read 64 entries at a time, one
+// per lane, as ListTiles does; the merge itself is wave-uniform scalar work.
+struct PairTiles {
+  const int32_t* bs;
+  const int32_t* la;
+  const int32_t* lb;
+  int ca, cb, basea, baseb, ka, kb;
+  int kt, kend, mask;
+  int sa_l, ea_l, sb_l, eb_l;  // per lane: bounds of blocks la[basea + lane], lb[baseb + lane]
+  __device__ __forceinline__ void fetch_a(int lane) {
+    const int i = basea + lane;
+    const int j = (i < ca) ? la[i] : 0;
+    sa_l = bs[j];
+    ea_l = bs[j + 1];
+  }
+  __device__ __forceinline__ void fetch_b(int lane) {
+    const int i = baseb + lane;
+    const int j = (i < cb) ? lb[i] : 0;
+    sb_l = bs[j];
+    eb_l = bs[j + 1];
+  }
+  // the next block: the smaller head of the two lists (block rows ascend with the block index)
+  __device__ __forceinline__ void pick() {
+    const bool va = basea + ka < ca, vb = baseb + kb < cb;
+    if (!va && !vb) {
+      mask = 0;
+      return;
+    }
+    const int sa = va ? __builtin_amdgcn_readlane(sa_l, ka) : INT_MAX;
+    const int sb = vb ? __builtin_amdgcn_readlane(sb_l, kb) : INT_MAX;
+    if (sa <= sb) {
+      kt = sa;
+      kend = __builtin_amdgcn_readlane(ea_l, ka);
+    } else {
+      kt = sb;
+      kend = __builtin_amdgcn_readlane(eb_l, kb);
+    }
+    mask = (sa <= sb ? 1 : 0) | (sb <= sa ? 2 : 0);
+  }
+  __device__ __forceinline__ void begin(const int32_t* a, int na, const int32_t* b, int nb, const int32_t* bounds, int lane) {
+    bs = bounds;
+    la = a;
+    lb = b;
+    ca = na;
+    cb = nb;
+    basea = baseb = ka = kb = 0;
+    kt = kend = 0;
+    if (ca > 0) fetch_a(lane);
+    if (cb > 0) fetch_b(lane);
+    pick();
+  }
+  __device__ __forceinline__ bool valid() const { return mask != 0; }
+  __device__ __forceinline__ void next(int lane) {
+    kt += 64;
+    if (kt < kend) return;
+    if (mask & 1) {
+      if (++ka == 64) {
+        basea += 64;
+        ka = 0;
+        if (basea < ca) fetch_a(lane);
+      }
+    }
+    if (mask & 2) {
+      if (++kb == 64) {
+        baseb += 64;
+        kb = 0;
+        if (baseb < cb) fetch_b(lane);
+      }
+    }
+    pick();
+  }
+};
+
+
+// The first rows of the two atoms of pair p (zone m = p / 4, slot s = p % 4).  In a zone of
+// 128- or 256-row blocks the pair is atoms 2s and 2s + 1 of the zone, which lie in one block
+// and share its list.  In a zone of eight 64-row blocks the blocks are matched greedily by the
+// size of the intersection of their lists (largest first; among equal sizes the pair (a, c),
+// a < c, that comes first in lexicographic order), counted on LDS bitmaps; slot s takes the
+// s-th pair chosen.  The matching depends only on the lists, so the zone's four workgroups
+// agree on it and every atom is in exactly one pair.  scratch: 8 * ceil(nbmax / 32) + 32 words
+// of LDS, free again when this returns.
+__device__ __forceinline__ void pair_atoms(const int32_t* bs, int nbmax, const int32_t* cnt_h, const int32_t* idx_h,
+                                           int p, uint32_t* scratch, int& rowA, int& rowB) {
+  const int tid = threadIdx.x;
+  const int m = p >> 2, s = p & 3;
+  const int j0 = block_of_row(bs, nbmax, 512 * m);
+  if (bs[j0 + 1] - bs[j0] > 64) {
+    rowA = 512 * m + 128 * s;
+    rowB = rowA + 64;
+    return;
+  }
+  const int nw = (nbmax + 31) >> 5;
+  uint32_t* bm = scratch;
+  int* inter = reinterpret_cast<int*>(scratch + 8 * nw);
+  for (int i = tid; i < 8 * nw; i += blockDim.x) bm[i] = 0u;
+  __syncthreads();
+  for (int q = 0; q < 8; ++q) {
+    const int c = cnt_h[j0 + q];
+    const int32_t* l = idx_h + (int64_t)(j0 + q) * nbmax;
+    for (int i = tid; i < c; i += blockDim.x) {
+      const int j = l[i];
+      atomicOr(&bm[q * nw + (j >> 5)], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  // 28 block pairs x 8 threads: popcounts of the AND of two bitmaps
+  {
+    const int pi = tid >> 3, sub = tid & 7;
+    int a = 0, n = pi;
+    while (a < 7 && n >= 7 - a) {
+      n -= 7 - a;
+      ++a;
+    }
+    const int c = a + 1 + n;
+    int cnt = 0;
+    if (pi < 28)
+      for (int wd = sub; wd < nw; wd += 8) cnt += __popc(bm[a * nw + wd] & bm[c * nw + wd]);
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 8);
+    if (pi < 28 && sub == 0) inter[pi] = cnt;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t used = 0u;
+    int ra = 0, rc = 1;
+    for (int k = 0; k <= s; ++k) {
+      int best = -1, n = 0;
+      for (int a2 = 0; a2 < 8; ++a2)
+        for (int c2 = a2 + 1; c2 < 8; ++c2, ++n)
+          if (!((used >> a2) & 1u) && !((used >> c2) & 1u) && inter[n] > best) {
+            best = inter[n];
+            ra = a2;
+            rc = c2;
+          }
+      used |= (1u << ra) | (1u << rc);
+    }
+    inter[28] = bs[j0 + ra];
+    inter[29] = bs[j0 + rc];
+  }
+  __syncthreads();
+  rowA = __builtin_amdgcn_readfirstlane(inter[28]);
+  rowB = __builtin_amdgcn_readfirstlane(inter[29]);
+  __syncthreads();
+}
+
+// Forward over a pair of atoms of one zone (pair_atoms) walking the union of their lists, so a
+// key tile both atoms selected is loaded once.  Workgroup = 4 waves; wave w owns rows 32*(w&1)..
+// of both atoms and keys 32*(w>>1).. of every staged tile, and computes each tile for each atom
+// that selected it, so every wave has work on every tile.  The first atom's Q rows are held in
+// registers, the second's are staged once in LDS (80 KB per workgroup with the two K/V stages:
+// two workgroups per CU).  The two waves sharing a row half keep separate online-softmax states
+// per atom, merged once at the end.
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -382,53 +536,64 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
   constexpr uint32_t SB = 4 * T;  // bytes of one stage (K tile, V tile)
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * T];  // two stages
+  // two stages, then the second atom's Q rows
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[5 * T];
+  const uint16_t* sQB = smem + 4 * T;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = w & 1, kh = w >> 1;
   const int h = blockIdx.y;
-  const int natoms = N >> 6;
-  const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
-  const int qb = block_of_row(bs, nbmax, row0);
+  int rowA, rowB;
+  pair_atoms(bs, nbmax, sel_count + (int64_t)h * nbmax, sel_idx + (int64_t)h * nbmax * nbmax,
+             xcd_atom(blockIdx.x, N >> 7), reinterpret_cast<uint32_t*>(smem), rowA, rowB);
+  const int qa = block_of_row(bs, nbmax, rowA), qb = block_of_row(bs, nbmax, rowB);
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
-  const int myrow = row0 + 32 * rh + l32;
+  const int myrow = rowA + 32 * rh + l32;  // this lane's row of the first atom
 
+  uint32_t doff[Tile<D>::NI], tav[2];
+  dma_offsets<D>(w, lane, doff);
+  dma_tile<D>(Q + hoff + (int64_t)rowB * D, smem + 4 * T, w, doff);
   bf16x8 qop[DS];
   {
     const uint16_t* qr = Q + hoff + (int64_t)myrow * D + (D / 2) * half;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 8 * s));
   }
-  f32x16 oacc[DB];
+  f32x16 oa[DB], ob[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = zero16();
-  float mrow = -INFINITY, lrow = 0.f;
+  for (int db = 0; db < DB; ++db) {
+    oa[db] = zero16();
+    ob[db] = zero16();
+  }
+  float ma = -INFINITY, la = 0.f, mb = -INFINITY, lb = 0.f;
 
-  ListTiles it;
-  it.begin(sel_idx + ((int64_t)h * nbmax + qb) * nbmax, bs, sel_count[(int64_t)h * nbmax + qb], lane);
-  uint32_t doff[Tile<D>::NI], tav[2];
-  dma_offsets<D>(w, lane, doff);
+  PairTiles it;
+  {
+    const int64_t ra = (int64_t)h * nbmax + qa, rb = (int64_t)h * nbmax + qb;
+    it.begin(sel_idx + ra * nbmax, sel_count[ra], sel_idx + rb * nbmax, sel_count[rb], bs, lane);
+  }
   tr_table<D>(smem, lane, 32 * kh, tav);
   // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
+  const uint32_t rowq = row_addr<D>(32 * rh + l32) ^ ((CH * half) << 4);
   auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
     uint16_t* s = smem + soff / 2;
     dma_tile<D>(Kh + (int64_t)it.kt * D, s, w, doff);
     dma_tile<D>(Vh + (int64_t)it.kt * D, s + T, w, doff);
   };
-  auto compute = [&]() __attribute__((always_inline)) {
+  // one atom's rows against the wave's 32 keys of the staged tile; FROM_LDS: Q rows from sQB
+  auto compute = [&](auto fromc, f32x16(&oacc)[DB], float& mrow, float& lrow) __attribute__((always_inline)) {
+    constexpr bool FROM_LDS = decltype(fromc)::value;
     const uint16_t* sK = smem;
-    // S^T = K Q^T for this wave's 32 keys x 32 rows
     f32x16 sacc = zero16();
 #pragma unroll
-    for (int st = 0; st < DS; ++st) sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qop[st], sacc);
-    // online softmax in base 2 (logits scaled by sm_scale * log2 e).  The running max, shared by
-    // the two lanes of a row (lane and lane ^ 32 hold 16 of the tile's 32 keys each), is raised
-    // and O rescaled only when a tile exceeds it by more than the slack, so the cross-lane max
-    // is formed only then; each lane keeps its own partial row sum, added up after the loop.
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 qv = FROM_LDS ? lds_b128(sQB, rowq ^ (st << 4)) : qop[st];
+      sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qv, sacc);
+    }
     float mx = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
@@ -449,7 +614,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
       psum += pv;
     }
     lrow += psum;
-    // O^T += V^T P^T, P as bf16 head + residual
     auto pv = [&](auto ttc) __attribute__((always_inline)) {
       constexpr int tt = decltype(ttc)::value;
       bf16x8 p_hi, p_lo, vt[DB];
@@ -461,8 +625,6 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
         oacc[db] = mfma(vt[db], p_lo, oacc[db]);
       }
     };
-    // the PV products are issued at raised wave priority, so that the other workgroup's wave on
-    // the SIMD, in its softmax or S phase, yields issue slots to them (measured: -1.5 %)
     __builtin_amdgcn_s_setprio(1);
     pv(std::integral_constant<int, 0>{});
     pv(std::integral_constant<int, 1>{});
@@ -474,10 +636,12 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
     while (true) {
       dma_wait();
       __syncthreads();
+      const int cur = it.mask;
       it.next(lane);
       const bool more = it.valid();
       if (more) stage(soff ^ SB);
-      compute();
+      if (cur & 1) compute(std::false_type{}, oa, ma, la);
+      if (cur & 2) compute(std::true_type{}, ob, mb, lb);
       if (!more) break;
       soff ^= SB;
       rowa ^= SB;
@@ -485,57 +649,69 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
       tav[0] += step;
       tav[1] += step;
     }
+  } else {
+    dma_wait();
   }
-  lrow += __shfl_xor(lrow, 32, 64);
-  // merge the key halves: the kh = 1 wave of each row half hands (O, m, l) over through LDS
+  la += __shfl_xor(la, 32, 64);
+  lb += __shfl_xor(lb, 32, 64);
+  // merge the key halves of both atoms: the kh = 1 wave of each row half hands (O, m, l) over
+  // through LDS
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(smem);                 // [rh][DB * 16][64 lanes]
-  float* xm = reinterpret_cast<float*>(smem + 2 * T);         // [rh][m | l][32 rows]
+  float* xo = reinterpret_cast<float*>(smem);                 // [atom][rh][DB * 16][64 lanes]
+  float* xm = reinterpret_cast<float*>(smem) + 4 * DB * 16 * 64;  // [atom][rh][m | l][32 rows]
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[((rh * DB + db) * 16 + r) * 64 + lane] = oacc[db][r];
+      for (int r = 0; r < 16; ++r) {
+        xo[(((0 * 2 + rh) * DB + db) * 16 + r) * 64 + lane] = oa[db][r];
+        xo[(((1 * 2 + rh) * DB + db) * 16 + r) * 64 + lane] = ob[db][r];
+      }
     if (half == 0) {
-      xm[rh * 64 + l32] = mrow;
-      xm[rh * 64 + 32 + l32] = lrow;
+      xm[(0 * 2 + rh) * 64 + l32] = ma;
+      xm[(0 * 2 + rh) * 64 + 32 + l32] = la;
+      xm[(1 * 2 + rh) * 64 + l32] = mb;
+      xm[(1 * 2 + rh) * 64 + 32 + l32] = lb;
     }
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = xm[rh * 64 + l32], l1 = xm[rh * 64 + 32 + l32];
-    const float m = fmaxf(mrow, m1);
-    const float a0 = (mrow == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrow - m);
-    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-    const float l = lrow * a0 + l1 * a1;
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    if (half == 0) LSE[(int64_t)h * N + myrow] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
-    // the lane holds O[myrow][d = 32db + 8jj + 4half + e]: O rounded to bf16 and, if requested,
-    // its rounding residual, 8 bytes per lane and store, in block or token order
-    const int64_t orw = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, myrow) * D + 4 * half;
-    uint16_t* orow = O + orw;
-    uint16_t* rrow = Olo ? Olo + orw : nullptr;
+    auto finish = [&](int at, const f32x16(&oacc)[DB], float mrow, float lrow) __attribute__((always_inline)) {
+      const int row = (at ? rowB : rowA) + 32 * rh + l32;
+      const float m1 = xm[(at * 2 + rh) * 64 + l32], l1 = xm[(at * 2 + rh) * 64 + 32 + l32];
+      const float m = fmaxf(mrow, m1);
+      const float a0 = (mrow == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrow - m);
+      const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      const float l = lrow * a0 + l1 * a1;
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      if (half == 0) LSE[(int64_t)h * N + row] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
+      const int64_t orw = out_row(rm, c_shapes, h / hpg, h, gridDim.y, N, row) * D + 4 * half;
+      uint16_t* orow = O + orw;
+      uint16_t* rrow = Olo ? Olo + orw : nullptr;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float ov[4], rv[4];
+        for (int jj = 0; jj < 4; ++jj) {
+          float ov[4], rv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * jj + e;
-          ov[e] = (oacc[db][r] * a0 + xo[((rh * DB + db) * 16 + r) * 64 + lane] * a1) * inv;
-          rv[e] = ov[e] - bf16_to_f32(f32_to_bf16(ov[e]));
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * jj + e;
+            ov[e] = (oacc[db][r] * a0 + xo[(((at * 2 + rh) * DB + db) * 16 + r) * 64 + lane] * a1) * inv;
+            rv[e] = ov[e] - bf16_to_f32(f32_to_bf16(ov[e]));
+          }
+          u32x2 pk;
+          pk[0] = pack_bf16x2(ov[0], ov[1]);
+          pk[1] = pack_bf16x2(ov[2], ov[3]);
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj) = pk;
+          if (rrow) {
+            pk[0] = pack_bf16x2(rv[0], rv[1]);
+            pk[1] = pack_bf16x2(rv[2], rv[3]);
+            *reinterpret_cast<u32x2*>(rrow + 32 * db + 8 * jj) = pk;
+          }
         }
-        u32x2 pk;
-        pk[0] = pack_bf16x2(ov[0], ov[1]);
-        pk[1] = pack_bf16x2(ov[2], ov[3]);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * jj) = pk;
-        if (rrow) {
-          pk[0] = pack_bf16x2(rv[0], rv[1]);
-          pk[1] = pack_bf16x2(rv[2], rv[3]);
-          *reinterpret_cast<u32x2*>(rrow + 32 * db + 8 * jj) = pk;
-        }
-      }
+    };
+    finish(0, oa, ma, la);
+    finish(1, ob, mb, lb);
   }
 }
 
@@ -891,7 +1067,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
                              const RowMap& out, hipStream_t st) {
-  dim3 grid((unsigned)(g.N / 64), g.heads);
+  dim3 grid((unsigned)(g.N / 128), g.heads);  // one workgroup per pair of atoms
   const float scale2 = sm_scale * kLog2e;
   KernelTrace tr("k_fwd", st);
   if (g.d == 64)
