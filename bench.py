@@ -399,6 +399,11 @@ def main():
     f_bwd = 2.5 * f_fwd
     attn_ms = stage_ms["bsa_fwd"] + stage_ms["bsa_bwd"]
     attn_tflops = (f_fwd + f_bwd) / (attn_ms * 1e-3) / 1e12
+    # matrix-core work actually issued per query-key pair (bf16 path): forward S and the two
+    # halves of the split PV product (3 products of 2d FLOP), dQ kernel S, dP and split dQ (4),
+    # dK/dV kernel S, dP, split dV and split dK (6): 26d against the algorithmic 14d
+    f_exec = 26.0 * d * pairs
+    attn_exec_tflops = f_exec / (attn_ms * 1e-3) / 1e12
     # algorithmic FLOPs per kernel: forward QK^T + PV; dK/dV kernel S, dP, dV, dK; dQ kernel
     # only its dQ product (its S and dP are recomputation beyond the five backward GEMMs)
     kflops = {"k_fwd": 4.0 * d * pairs, "k_dkdv": 8.0 * d * pairs, "k_dq": 2.0 * d * pairs}
@@ -494,6 +499,11 @@ def main():
         "attn_fwd_bwd_ms": round(attn_ms, 3),
         "attn_tflops": round(attn_tflops, 1),
         "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_executed_mfma": ({"TFLOP/s": round(attn_exec_tflops, 1),
+                                "frac": round(attn_exec_tflops / PEAK_BF16_TFLOPS, 4),
+                                "note": "matrix-core FLOPs issued: split-bf16 P and dS products and the dQ "
+                                        "kernel's recomputed S and dP included (26d per pair against 14d)"}
+                               if cfg.dtype == "bf16" else None),
         "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
         "kernel_ms": {kn: round(kern_ms[kn], 4) for kn in MFMA_KERNELS},
         "attn_kernels": attn_k,
