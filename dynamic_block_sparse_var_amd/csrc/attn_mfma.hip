@@ -411,7 +411,8 @@ struct PairTiles {
     }
     mask = (sa <= sb ? 1 : 0) | (sb <= sa ? 2 : 0);
   }
-  __device__ __forceinline__ void begin(const int32_t* a, int na, const int32_t* b, int nb, const int32_t* bounds, int lane) {
+  __device__ __forceinline__ void begin(const int32_t* a, int na, const int32_t* b, int nb, const int32_t* bounds,
+                                        int lane) {
     bs = bounds;
     la = a;
     lb = b;
@@ -444,7 +445,6 @@ struct PairTiles {
     pick();
   }
 };
-
 
 // The first rows of the two atoms of pair p (zone m = p / 4, slot s = p % 4).  In a zone of
 // 128- or 256-row blocks the pair is atoms 2s and 2s + 1 of the zone, which lie in one block
