@@ -6,9 +6,8 @@
 // the plain-precision path for fp32 inputs, not tuned.
 //
 // Backward helpers shared by both paths:
-//   k_fill_u32   zero fill (used instead of a memset so the call stays graph-capturable),
-//   k_mask_t     transposed selection bitmap: bit i of word [h][j][i/32] set when j in S_i,
-//                built with atomicOr (order-independent, so deterministic),
+//   k_mask_t     transposed selection bitmap: bit i of word [h][j][i/32] set when j in S_i;
+//                every word is written exactly once (no clearing pass), deterministically,
 //   k_delta      delta_r = dO_r . O_r in fp32.
 #include <math.h>
 
@@ -171,25 +170,31 @@ __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const 
   }
 }
 
-__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t val) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = val;
-}
+constexpr int kMaskColMax = 8 * kMaxZones;  // NBMAX bound: one 32 KB LDS column of mask words
 
+// One workgroup per (word column w, head): the lists of query blocks 32w..32w+31 are ORed into
+// an LDS column of NBMAX words (bit b of word j: block j is in the list of query block 32w + b,
+// LDS atomics, order-free), which is then written out: word [h][j][w] for every j, once.
 __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int nw, int hpg,
                                                 int64_t N) {
-  const int i = blockIdx.x, h = blockIdx.y;
+  __shared__ uint32_t col[kMaskColMax];
+  const int w = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
-  if (bs[i] >= N) return;
-  const int64_t row = (int64_t)h * nbmax + i;
-  const int cnt = sel_count[row];
-  const int32_t* list = sel_idx + row * nbmax;
-  for (int s = threadIdx.x; s < cnt; s += 256) {
-    const int j = list[s];
-    atomicOr(&mask_t[((int64_t)h * nbmax + j) * nw + (i >> 5)], 1u << (i & 31));
+  for (int j = tid; j < nbmax; j += blockDim.x) col[j] = 0u;
+  __syncthreads();
+  for (int b = 0; b < 32; ++b) {
+    const int i = 32 * w + b;
+    if (i >= nbmax || bs[i] >= N) break;  // past the group's blocks
+    const int64_t row = (int64_t)h * nbmax + i;
+    const int cnt = sel_count[row];
+    const int32_t* list = sel_idx + row * nbmax;
+    for (int s = tid; s < cnt; s += blockDim.x) atomicOr(&col[list[s]], 1u << b);
   }
+  __syncthreads();
+  uint32_t* out = mask_t + (int64_t)h * nbmax * nw + w;
+  for (int j = tid; j < nbmax; j += blockDim.x) out[(int64_t)j * nw] = col[j];
 }
 
 // delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step.  O = o + o_lo when the
@@ -296,14 +301,10 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   float* lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + w.lse2_off);
   uint32_t* mask_t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + w.mask_off);
   // transposed selection
-  const int fill_blocks = (int)((w.mask_words + 255) / 256 < 4096 ? (w.mask_words + 255) / 256 : 4096);
-  hipLaunchKernelGGL(k_fill_u32, dim3(fill_blocks > 0 ? fill_blocks : 1), dim3(256), 0, st, mask_t,
-                     (int64_t)w.mask_words, 0u);
-  prism_status s = check_launch("k_fill_u32");
-  if (s != PRISM_OK) return s;
-  hipLaunchKernelGGL(k_mask_t, dim3(g.nbmax, g.heads), dim3(256), 0, st, mask_t, bs, cnt, idx, g.nbmax, w.nw, g.hpg,
+  if (g.nbmax > kMaskColMax) return fail(PRISM_E_RANGE, "transposed selection: more than %d blocks", kMaskColMax);
+  hipLaunchKernelGGL(k_mask_t, dim3(w.nw, g.heads), dim3(256), 0, st, mask_t, bs, cnt, idx, g.nbmax, w.nw, g.hpg,
                      g.N);
-  s = check_launch("k_mask_t");
+  prism_status s = check_launch("k_mask_t");
   if (s != PRISM_OK) return s;
   // delta
   const int64_t rows = (int64_t)g.heads * g.N;
