@@ -154,6 +154,43 @@ def test_attention_backward(run):
         assert_close_attn(name, f64(mine), oracle.unpermute(ref, o["pos"], c.heads))
 
 
+def test_empty_lists(run):
+    """Query blocks with an empty list (possible through the C ABI with a caller's selection):
+    their rows get O = 0 and LSE = -inf, zero dQ and no share in dK, dV; every other row is
+    unchanged.  Blocks i with i % 5 in {1, 2} are emptied, which leaves atom pairs of the
+    forward with one empty and one non-empty list as well as pairs with both lists empty."""
+    c, o = run.cfg, run.orc
+    run.inject_oracle_plan()
+    L = run.layer
+    from dynamic_block_sparse_var_amd import prism_permute
+
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    cnt = o["sel_count"].copy()
+    blk = np.arange(cnt.shape[1])
+    cnt[:, (blk % 5 == 1) | (blk % 5 == 2)] = 0
+    L.sel_count.copy_(torch.from_numpy(cnt))
+    L.sel_idx.copy_(torch.from_numpy(o["sel_idx"]))
+    L.attend(c.sm_scale)
+    if run.backward:
+        L.backward(run.dout, c.sm_scale)
+    torch.cuda.synchronize()
+    vp = oracle.permute(run.inp["v"], o["pos"], c.heads)
+    of, lf = oracle.attn_fwd(o["qp"], o["kp"], vp, o["block_start"], o["nblocks"], c.groups, cnt, o["sel_idx"],
+                             c.sm_scale)
+    assert_close_attn("O (empty lists)", f64(L.o), oracle.unpermute(of, o["pos"], c.heads))
+    lse = L.lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lf)
+    assert (~fin).any(), "no row had an empty list"
+    assert np.isneginf(lse[~fin]).all()
+    assert np.abs(lse[fin] - lf[fin]).max() <= LSE_ABS
+    if run.backward:
+        dop = oracle.permute(run.inp["dout"], o["pos"], c.heads)
+        ob = oracle.attn_bwd(o["qp"], o["kp"], vp, dop, o["block_start"], o["nblocks"], c.groups, cnt,
+                             o["sel_idx"], c.sm_scale)
+        for name, mine, ref in (("dQ", L.dq, ob["dq"]), ("dK", L.dk, ob["dk"]), ("dV", L.dv, ob["dv"])):
+            assert_close_attn(name + " (empty lists)", f64(mine), oracle.unpermute(ref, o["pos"], c.heads))
+
+
 def test_deterministic(run):
     _gpu_attention(run)
     L = run.layer
