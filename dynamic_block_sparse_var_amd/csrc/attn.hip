@@ -8,7 +8,9 @@
 // Backward helpers shared by both paths:
 //   k_mask_t     transposed selection bitmap: bit i of word [h][j][i/32] set when j in S_i;
 //                every word is written exactly once (no clearing pass), deterministically,
-//   k_delta      delta_r = dO_r . O_r in fp32.
+//   k_delta      delta_r = dO_r . O_r in fp32,
+//   k_atom_work, k_launch_order
+//                the launch orders of the matrix-core dQ and dK/dV kernels (heavy atoms first).
 #include <math.h>
 
 #include "attn_common.h"
@@ -197,6 +199,83 @@ __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, c
   for (int j = tid; j < nbmax; j += blockDim.x) out[(int64_t)j * nw] = col[j];
 }
 
+
+// Work estimates for the launch orders of the matrix-core backward, per (head, atom): the
+// length of the atom's query-block list (the blocks dQ walks) and the number of query blocks
+// whose lists hold the atom's key block (the set bits of its transposed-selection row, the
+// blocks dK/dV walks).  One wave per (block, head).
+__global__ __launch_bounds__(64) void k_atom_work(int32_t* __restrict__ work_q, int32_t* __restrict__ work_k,
+                                                  const uint32_t* __restrict__ mask_t,
+                                                  const int32_t* __restrict__ block_start,
+                                                  const int32_t* __restrict__ sel_count, int nbmax, int nw, int hpg,
+                                                  int64_t N) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  if (bs[i] >= N) return;
+  const uint32_t* row = mask_t + ((int64_t)h * nbmax + i) * nw;
+  int c = 0;
+  for (int w = lane; w < nw; w += 64) c += __popc(row[w]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  const int q = sel_count[(int64_t)h * nbmax + i];
+  const int64_t base = (int64_t)h * (N >> 6);
+  for (int a = (bs[i] >> 6) + lane; a < (bs[i + 1] >> 6); a += 64) {
+    work_q[base + a] = q;
+    work_k[base + a] = c;
+  }
+}
+
+// Launch order of a matrix-core backward kernel (workgroup 0: dQ, 1: dK/dV).  Item = head *
+// natoms + atom; the unordered launch runs head by head, atoms in xcd_atom order.  A few query
+// blocks have Top-p-extended lists several times longer than the rest (and their key blocks
+// are selected by many more query blocks); launched in place they can start near the end of
+// the launch and hold it open long after the other workgroups are done.  So the items whose
+// work exceeds 1.5x the mean go first; both parts keep the unordered relative order, which
+// keeps the neighbouring atoms that share tiles together on one XCD.  Deterministic.
+__global__ __launch_bounds__(1024) void k_launch_order(int32_t* __restrict__ order, const int32_t* __restrict__ work,
+                                                       int heads, int natoms) {
+  __shared__ int part[1024];
+  __shared__ unsigned long long tot;
+  const int tid = threadIdx.x, side = blockIdx.x;
+  const int n = heads * natoms;
+  int32_t* ord = order + (int64_t)side * n;
+  const int32_t* wk = work + (int64_t)side * n;
+  auto item_at = [&](int t) { return (t / natoms) * natoms + xcd_atom(t % natoms, natoms); };
+  if (tid == 0) tot = 0ull;
+  __syncthreads();
+  const int per = (n + 1023) / 1024;
+  const int t0 = min(n, tid * per), t1 = min(n, t0 + per);
+  unsigned long long sum = 0ull;
+  for (int t = t0; t < t1; ++t) sum += (unsigned long long)wk[item_at(t)];
+  atomicAdd(&tot, sum);
+  __syncthreads();
+  // heavy: 2 * work * n > 3 * total, i.e. work > 1.5 * mean, in integers
+  const unsigned long long total = tot;
+  auto heavy = [&](int t) { return 2ull * (unsigned long long)wk[item_at(t)] * (unsigned long long)n > 3ull * total; };
+  int c = 0;
+  for (int t = t0; t < t1; ++t) c += heavy(t);
+  part[tid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    tot = (unsigned long long)run;
+  }
+  __syncthreads();
+  const int nheavy = (int)tot;
+  int ph = part[tid], pl = nheavy + (t0 - part[tid]);
+  for (int t = t0; t < t1; ++t) {
+    if (heavy(t))
+      ord[ph++] = item_at(t);
+    else
+      ord[pl++] = item_at(t);
+  }
+}
+
 // delta = rowsum(dO * O): LPR lanes per row, 16 bytes per lane per step.  O = o + o_lo when the
 // forward stored its rounding residual; o and o_lo are read in block or token order (om), dO in
 // block order.  Also lse2 = LSE * log2(e), the row statistic in the base-2 units the
@@ -278,7 +357,11 @@ BwdWorkspace bwd_workspace_layout(const Geom& g) {
   w.mask_off = 2 * delta_bytes;
   const size_t mask_words = (size_t)g.heads * g.nbmax * w.nw;
   w.mask_words = mask_words;
-  w.total = w.mask_off + ((mask_words * sizeof(uint32_t) + 255) & ~(size_t)255);
+  w.order_off = w.mask_off + ((mask_words * sizeof(uint32_t) + 255) & ~(size_t)255);
+  w.items = (int)(g.heads * (g.N / 64));
+  const size_t pair_bytes = ((size_t)2 * w.items * sizeof(int32_t) + 255) & ~(size_t)255;
+  w.work_off = w.order_off + pair_bytes;
+  w.total = w.work_off + pair_bytes;
   return w;
 }
 
@@ -306,6 +389,18 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
                      g.N);
   prism_status s = check_launch("k_mask_t");
   if (s != PRISM_OK) return s;
+  // launch orders of the matrix-core kernels
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + w.order_off);
+  if (g.bf16) {
+    int32_t* work = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + w.work_off);
+    hipLaunchKernelGGL(k_atom_work, dim3(g.nbmax, g.heads), dim3(64), 0, st, work, work + w.items, mask_t, bs, cnt,
+                       g.nbmax, w.nw, g.hpg, g.N);
+    s = check_launch("k_atom_work");
+    if (s != PRISM_OK) return s;
+    hipLaunchKernelGGL(k_launch_order, dim3(2), dim3(1024), 0, st, order, work, g.heads, (int)(g.N / 64));
+    s = check_launch("k_launch_order");
+    if (s != PRISM_OK) return s;
+  }
   // delta
   const int64_t rows = (int64_t)g.heads * g.N;
   const int lpr = g.d * g.esize / 16;
@@ -328,7 +423,8 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   s = check_launch("k_delta");
   if (s != PRISM_OK) return s;
   if (g.bf16)
-    return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse2, delta, mask_t, w.nw, dq, dk, dv, out, st);
+    return launch_mfma_bwd(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse2, delta, mask_t, w.nw, order,
+                           order + w.items, dq, dk, dv, out, st);
   if (g.d == 64)
     return run_ref_bwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, dout, lse, delta, mask_t, w.nw, dq, dk, dv, out,
                                   st);

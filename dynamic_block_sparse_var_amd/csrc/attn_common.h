@@ -5,13 +5,21 @@
 
 namespace prism {
 
-// Backward workspace: delta [heads, N] fp32, lse2 = LSE * log2(e) [heads, N] fp32, then the
-// transposed selection bitmap [heads, NBMAX, nw] uint32 (nw = ceil(NBMAX / 32)), each 256-byte
+// Backward workspace: delta [heads, N] fp32, lse2 = LSE * log2(e) [heads, N] fp32, the
+// transposed selection bitmap [heads, NBMAX, nw] uint32 (nw = ceil(NBMAX / 32)), then for the
+// matrix-core dQ and dK/dV kernels their launch orders [2][items] int32 and the per-atom work
+// estimates the orders are built from [2][items] int32 (items = heads * N / 64), each 256-byte
 // aligned.
 struct BwdWorkspace {
-  size_t delta_off, lse2_off, mask_off, mask_words, total;
-  int nw;
+  size_t delta_off, lse2_off, mask_off, mask_words, order_off, work_off, total;
+  int nw, items;
 };
+
+// Atoms of one head in launch order, spread so that each XCD (workgroup id mod 8) walks a
+// contiguous range: launch position x of a head's natoms workgroups takes atom xcd_atom(x).
+__device__ __forceinline__ int xcd_atom(int x, int natoms) {
+  return ((natoms & 7) == 0) ? (x & 7) * (natoms >> 3) + (x >> 3) : x;
+}
 BwdWorkspace bwd_workspace_layout(const Geom& g);
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
@@ -19,7 +27,8 @@ prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cn
                              float* lse, const RowMap& out, hipStream_t st);
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, const void* dout,
-                             const float* lse2, const float* delta, const uint32_t* mask_t, int nw, float* dq,
-                             float* dk, float* dv, const RowMap& out, hipStream_t st);
+                             const float* lse2, const float* delta, const uint32_t* mask_t, int nw,
+                             const int32_t* order_q, const int32_t* order_k, float* dq, float* dk, float* dv,
+                             const RowMap& out, hipStream_t st);
 
 }  // namespace prism

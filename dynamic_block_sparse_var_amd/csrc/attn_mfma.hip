@@ -108,11 +108,6 @@ __device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
-// atoms of one head, spread so that each XCD (workgroup id mod 8) walks a contiguous range
-__device__ __forceinline__ int xcd_atom(int bid, int natoms) {
-  return ((natoms & 7) == 0) ? (bid & 7) * (natoms >> 3) + (bid >> 3) : bid;
-}
-
 // ---- swizzled, unpadded 64 x D tiles filled by direct global -> LDS loads -----------------
 //
 // Row r occupies 2*D contiguous bytes; its 16-byte chunk c sits in chunk slot c ^ swz(r).  The
@@ -726,7 +721,8 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
                                                const float* __restrict__ LSE2, const float* __restrict__ delta,
                                                float* __restrict__ dQ, const int32_t* __restrict__ block_start,
                                                const int32_t* __restrict__ sel_count,
-                                               const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
+                                               const int32_t* __restrict__ sel_idx,
+                                               const int32_t* __restrict__ order, int nbmax, int hpg, int N,
                                                float scale2, float sm_scale, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
@@ -735,9 +731,11 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = w & 1, kh = w >> 1;
-  const int h = blockIdx.y;
+  // this workgroup's item of the launch order: (head, atom) = divmod(item, natoms)
   const int natoms = N >> 6;
-  const int row0 = xcd_atom(blockIdx.x, natoms) * 64;
+  const int item = order[blockIdx.y * gridDim.x + blockIdx.x];
+  const int h = item / natoms;
+  const int row0 = (item - h * natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int qb = block_of_row(bs, nbmax, row0);
   const int64_t hoff = (int64_t)h * N * D;
@@ -876,7 +874,8 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
                                                  const float* __restrict__ LSE2, const float* __restrict__ delta,
                                                  float* __restrict__ dK, float* __restrict__ dV,
                                                  const int32_t* __restrict__ block_start,
-                                                 const uint32_t* __restrict__ mask_t, int nbmax, int nw, int hpg,
+                                                 const uint32_t* __restrict__ mask_t,
+                                                 const int32_t* __restrict__ order, int nbmax, int nw, int hpg,
                                                  int N, float scale2, float sm_scale, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
@@ -887,9 +886,11 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = w & 1, qh = w >> 1;
-  const int h = blockIdx.y;
+  // this workgroup's item of the launch order: (head, key atom) = divmod(item, natoms)
   const int natoms = N >> 6;
-  const int key0 = xcd_atom(blockIdx.x, natoms) * 64;
+  const int item = order[blockIdx.y * gridDim.x + blockIdx.x];
+  const int h = item / natoms;
+  const int key0 = (item - h * natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   const int kb_idx = block_of_row(bs, nbmax, key0);
   const int64_t hoff = (int64_t)h * N * D;
@@ -1083,32 +1084,33 @@ prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cn
 
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, const void* dout, const float* lse2,
-                             const float* delta, const uint32_t* mask_t, int nw, float* dq, float* dk, float* dv,
-                             const RowMap& out, hipStream_t st) {
+                             const float* delta, const uint32_t* mask_t, int nw, const int32_t* order_q,
+                             const int32_t* order_k, float* dq, float* dk, float* dv, const RowMap& out,
+                             hipStream_t st) {
   dim3 grid((unsigned)(g.N / 64), g.heads);
   const float scale2 = sm_scale * kLog2e;
   {
     KernelTrace tr("k_dq", st);
     if (g.d == 64)
       hipLaunchKernelGGL(k_dq<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
-                         (int)g.N, scale2, sm_scale, out);
+                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, order_q,
+                         g.nbmax, g.hpg, (int)g.N, scale2, sm_scale, out);
     else
       hipLaunchKernelGGL(k_dq<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, g.nbmax, g.hpg,
-                         (int)g.N, scale2, sm_scale, out);
+                         (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dq, bs, cnt, idx, order_q,
+                         g.nbmax, g.hpg, (int)g.N, scale2, sm_scale, out);
   }
   prism_status s = check_launch("k_dq");
   if (s != PRISM_OK) return s;
   KernelTrace tr("k_dkdv", st);
   if (g.d == 64)
     hipLaunchKernelGGL(k_dkdv<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
-                       g.hpg, (int)g.N, scale2, sm_scale, out);
+                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, order_k,
+                       g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale, out);
   else
     hipLaunchKernelGGL(k_dkdv<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, g.nbmax, nw,
-                       g.hpg, (int)g.N, scale2, sm_scale, out);
+                       (const uint16_t*)v, (const uint16_t*)dout, lse2, delta, dk, dv, bs, mask_t, order_k,
+                       g.nbmax, nw, g.hpg, (int)g.N, scale2, sm_scale, out);
   return check_launch("k_dkdv");
 }
 
