@@ -328,7 +328,7 @@ def main():
                                   L.sel_idx)
             mark(4)
             P.prism_bsa_fwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
-                                L.o_lo, L.lse)
+                                L.o_lo, L.lse, L.fwd_workspace)
             mark(5)
             P.prism_bsa_bwd_tok(pb, L.shape_idx, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.o,
                                 L.o_lo, do, L.lse, L.dq, L.dk, L.dv, L.workspace)
@@ -341,7 +341,8 @@ def main():
         P.prism_select_blocks(pb, L.block_start, L.qbar, L.kbar, sm, k_abs, k_frac, cfg.p, L.sel_count,
                               L.sel_idx)
         mark(5)
-        P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse)
+        P.prism_bsa_fwd(pb, L.block_start, L.sel_count, L.sel_idx, sm, L.qp, L.kp, L.vp, L.op, L.op_lo, L.lse,
+                        L.fwd_workspace)
         mark(6)
         P.prism_permute(pb, L.shape_idx, 1, [L.op], [L.o])
         mark(7)

@@ -86,14 +86,17 @@ def lib():
         "prism_permute": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp, _vp]),
         "prism_pool_blocks": (_i32, [_PB, _vp, _i32, _vp, _vp, _vp]),
         "prism_select_blocks": (_i32, [_PB, _vp, _vp, _vp, _f32, _i32, _f64, _f64, _vp, _vp, _vp]),
-        "prism_bsa_fwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "prism_bsa_fwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
+        "prism_bsa_fwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                 _vp]),
         "prism_bsa_bwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
         "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
         "prism_audio_norms": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp]),
         "prism_permute_pool": (_i32, [_PB, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
-        "prism_bsa_fwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+        "prism_bsa_fwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]),
         "prism_bsa_bwd_tok_workspace_bytes": (ctypes.c_size_t, [_PB]),
         "prism_bsa_bwd_tok": (_i32, [_PB, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, _vp]),
@@ -199,9 +202,21 @@ def prism_select_blocks(pb, block_start, qbar, kbar, sm_scale, k_abs, k_frac, p,
            "prism_select_blocks")
 
 
-def prism_bsa_fwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, stream=None):
+def prism_bsa_fwd_workspace_bytes(pb) -> int:
+    return int(lib().prism_bsa_fwd_workspace_bytes(ctypes.byref(pb)))
+
+
+def _ws(workspace):
+    """(pointer, bytes) of an optional workspace tensor."""
+    if workspace is None:
+        return None, 0
+    return _p(workspace), workspace.numel() * workspace.element_size()
+
+
+def prism_bsa_fwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
     _check(lib().prism_bsa_fwd(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale, _p(q), _p(k),
-                               _p(v), _p(o), _p(o_lo), _p(lse), _stream(stream)), "prism_bsa_fwd")
+                               _p(v), _p(o), _p(o_lo), _p(lse), wp, wn, _stream(stream)), "prism_bsa_fwd")
 
 
 def prism_bsa_bwd_workspace_bytes(pb) -> int:
@@ -216,10 +231,12 @@ def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_l
                                nbytes, _stream(stream)), "prism_bsa_bwd")
 
 
-def prism_bsa_fwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, stream=None):
+def prism_bsa_fwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, workspace=None,
+                      stream=None):
+    wp, wn = _ws(workspace)
     _check(lib().prism_bsa_fwd_tok(ctypes.byref(pb), _p(shape_idx), _p(block_start), _p(sel_count), _p(sel_idx),
-                                   sm_scale, _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(lse), _stream(stream)),
-           "prism_bsa_fwd_tok")
+                                   sm_scale, _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(lse), wp, wn,
+                                   _stream(stream)), "prism_bsa_fwd_tok")
 
 
 def prism_bsa_bwd_tok_workspace_bytes(pb) -> int:
@@ -279,6 +296,9 @@ class PrismLayer:
         self.sel_idx = torch.empty(H_, NB, NB, dtype=torch.int32, **e)
         self.lse = torch.empty(H_, N, dtype=torch.float32, **e)
         self.o = torch.empty(N, H_, d, dtype=dt, **e)
+        # the forward's launch order (heaviest pairs of atoms first); none for fp32 problems
+        fbytes = prism_bsa_fwd_workspace_bytes(pb)
+        self.fwd_workspace = torch.empty(fbytes, dtype=torch.uint8, **e) if fbytes > 0 else None
         # rounding residual of O (bf16 only), kept for an accurate backward
         keep_lo = backward and pb.dtype == BF16
         if token_io:
@@ -327,10 +347,10 @@ class PrismLayer:
         pb = self.pb
         if self.token_io:
             prism_bsa_fwd_tok(pb, self.shape_idx, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp,
-                              self.kp, self.vp, self.o, self.o_lo, self.lse, stream)
+                              self.kp, self.vp, self.o, self.o_lo, self.lse, self.fwd_workspace, stream)
             return self.o
         prism_bsa_fwd(pb, self.block_start, self.sel_count, self.sel_idx, sm_scale, self.qp, self.kp, self.vp,
-                      self.op, self.op_lo, self.lse, stream)
+                      self.op, self.op_lo, self.lse, self.fwd_workspace, stream)
         prism_permute(pb, self.shape_idx, 1, [self.op], [self.o], stream)
         return self.o
 

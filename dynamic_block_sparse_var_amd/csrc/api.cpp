@@ -283,9 +283,26 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
                        (hipStream_t)stream);
 }
 
+size_t prism_bsa_fwd_workspace_bytes(const prism_problem* pb) {
+  if (validate_problem(pb) != PRISM_OK) return 0;
+  Geom gm = make_geom(pb);
+  return bsa_fwd_workspace_bytes(gm);
+}
+
+// the optional forward workspace: NULL, or aligned and large enough
+static prism_status check_fwd_workspace(const Geom& gm, const void* workspace, size_t workspace_bytes) {
+  if (!workspace) return PRISM_OK;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(PRISM_E_ALIGN, "workspace not 256-byte aligned");
+  const size_t need = bsa_fwd_workspace_bytes(gm);
+  if (workspace_bytes < need)
+    return fail(PRISM_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return PRISM_OK;
+}
+
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start, const int32_t* sel_count,
                            const int32_t* sel_idx, float sm_scale, const void* q, const void* k, const void* v,
-                           void* o, void* o_lo, float* lse, void* stream) {
+                           void* o, void* o_lo, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   g_err[0] = 0;
   PRISM_TRY(validate_problem(pb));
   PRISM_TRY(need_aligned(block_start, "block_start"));
@@ -300,8 +317,9 @@ prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start, 
   if (!(sm_scale > 0.f) || !isfinite(sm_scale))
     return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
   Geom gm = make_geom(pb);
+  PRISM_TRY(check_fwd_workspace(gm, workspace, workspace_bytes));
   return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, lse,
-                        block_rows(), (hipStream_t)stream);
+                        workspace, block_rows(), (hipStream_t)stream);
 }
 
 size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb) {
@@ -345,7 +363,8 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, 
 
 prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
                                const int32_t* sel_count, const int32_t* sel_idx, float sm_scale, const void* q,
-                               const void* k, const void* v, void* o, void* o_lo, float* lse, void* stream) {
+                               const void* k, const void* v, void* o, void* o_lo, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   PRISM_TRY(validate_problem(pb));
   PRISM_TRY(need_aligned(shape_idx, "shape_idx"));
@@ -361,8 +380,9 @@ prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx
   if (!(sm_scale > 0.f) || !isfinite(sm_scale))
     return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
   Geom gm = make_geom(pb);
+  PRISM_TRY(check_fwd_workspace(gm, workspace, workspace_bytes));
   return launch_bsa_fwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, lse,
-                        token_rows(gm, shape_idx), (hipStream_t)stream);
+                        workspace, token_rows(gm, shape_idx), (hipStream_t)stream);
 }
 
 // the block-order backward workspace, then a block-order copy of dO

@@ -225,13 +225,14 @@ __global__ __launch_bounds__(64) void k_atom_work(int32_t* __restrict__ work_q, 
   }
 }
 
-// Launch order of a matrix-core backward kernel (workgroup 0: dQ, 1: dK/dV).  Item = head *
-// natoms + atom; the unordered launch runs head by head, atoms in xcd_atom order.  A few query
-// blocks have Top-p-extended lists several times longer than the rest (and their key blocks
-// are selected by many more query blocks); launched in place they can start near the end of
-// the launch and hold it open long after the other workgroups are done.  So the items whose
-// work exceeds 1.5x the mean go first; both parts keep the unordered relative order, which
-// keeps the neighbouring atoms that share tiles together on one XCD.  Deterministic.
+// Launch order of a matrix-core attention kernel; workgroup s orders item set s (the backward:
+// 0 dQ, 1 dK/dV; the forward: its pairs of atoms).  Item = head * natoms + unit (atom or pair);
+// the unordered launch runs head by head, units in xcd_atom order.  A few query blocks have
+// Top-p-extended lists several times longer than the rest (and their key blocks are selected by
+// many more query blocks); launched in place they can start near the end of the launch and hold
+// it open long after the other workgroups are done.  So the items whose work exceeds 1.5x the
+// mean go first; both parts keep the unordered relative order, which keeps the neighbouring
+// units that share tiles together on one XCD.  Deterministic.
 __global__ __launch_bounds__(1024) void k_launch_order(int32_t* __restrict__ order, const int32_t* __restrict__ work,
                                                        int heads, int natoms) {
   __shared__ int part[1024];
@@ -273,6 +274,29 @@ __global__ __launch_bounds__(1024) void k_launch_order(int32_t* __restrict__ ord
       ord[ph++] = item_at(t);
     else
       ord[pl++] = item_at(t);
+  }
+}
+
+
+// Work estimates for the forward's launch order, per (head, pair of atoms): in a zone of 64-row
+// blocks twice the longest list among the zone's blocks (the forward matches the blocks into
+// pairs itself, so each of the zone's four pairs gets the zone's worst case), in a zone of 128-
+// or 256-row blocks twice the list length of the pair's block.  One wave per (zone, head).
+__global__ __launch_bounds__(64) void k_pair_work(int32_t* __restrict__ work, const int32_t* __restrict__ block_start,
+                                                  const int32_t* __restrict__ sel_count, int nbmax, int hpg, int Z) {
+  const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  const int32_t* c = sel_count + (int64_t)h * nbmax;
+  const int j0 = block_of_row(bs, nbmax, kZoneVol * m);
+  const int B = bs[j0 + 1] - bs[j0];
+  if (lane < 4) {
+    int w = 0;
+    if (B == 64) {
+      for (int q = 0; q < 8; ++q) w = max(w, c[j0 + q]);
+    } else {
+      w = c[j0 + (128 * lane) / B];
+    }
+    work[((int64_t)h * Z + m) * 4 + lane] = 2 * w;
   }
 }
 
@@ -367,10 +391,31 @@ BwdWorkspace bwd_workspace_layout(const Geom& g) {
 
 size_t bsa_bwd_workspace_bytes(const Geom& g) { return bwd_workspace_layout(g).total; }
 
+// Forward workspace: its launch order [items] int32, then the work estimates [items] int32,
+// items = heads * N / 128 (pairs of atoms), each 256-byte aligned.
+static size_t fwd_items_bytes(const Geom& g) {
+  return ((size_t)g.heads * (size_t)(g.N / 128) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+size_t bsa_fwd_workspace_bytes(const Geom& g) { return g.bf16 ? 2 * fwd_items_bytes(g) : 0; }
+
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                             const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
-                            const RowMap& out, hipStream_t st) {
-  if (g.bf16) return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, o_lo, lse, out, st);
+                            void* ws, const RowMap& out, hipStream_t st) {
+  if (g.bf16) {
+    int32_t* order = nullptr;
+    if (ws) {
+      // launch order: pairs of atoms with the longest lists first
+      order = static_cast<int32_t*>(ws);
+      int32_t* work = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + fwd_items_bytes(g));
+      hipLaunchKernelGGL(k_pair_work, dim3(g.Z, g.heads), dim3(64), 0, st, work, bs, cnt, g.nbmax, g.hpg, g.Z);
+      prism_status s = check_launch("k_pair_work");
+      if (s != PRISM_OK) return s;
+      hipLaunchKernelGGL(k_launch_order, dim3(1), dim3(1024), 0, st, order, work, g.heads, (int)(g.N / 128));
+      s = check_launch("k_launch_order");
+      if (s != PRISM_OK) return s;
+    }
+    return launch_mfma_fwd(g, bs, cnt, idx, sm_scale, q, k, v, o, o_lo, lse, order, out, st);
+  }
   if (g.d == 64) return run_ref_fwd<float, 64>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, out, st);
   return run_ref_fwd<float, 128>(g, bs, cnt, idx, sm_scale, q, k, v, o, lse, out, st);
 }

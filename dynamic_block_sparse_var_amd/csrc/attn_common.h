@@ -22,9 +22,10 @@ __device__ __forceinline__ int xcd_atom(int x, int natoms) {
 }
 BwdWorkspace bwd_workspace_layout(const Geom& g);
 
+// order: NULL (plain launch order) or the forward's launch order, items = head * N/128 + pair
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, void* o, void* o_lo,
-                             float* lse, const RowMap& out, hipStream_t st);
+                             float* lse, const int32_t* order, const RowMap& out, hipStream_t st);
 prism_status launch_mfma_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx,
                              float sm_scale, const void* q, const void* k, const void* v, const void* dout,
                              const float* lse2, const float* delta, const uint32_t* mask_t, int nw,

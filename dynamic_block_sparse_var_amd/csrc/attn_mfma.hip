@@ -526,7 +526,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
                                                 uint16_t* __restrict__ Olo, float* __restrict__ LSE,
                                                 const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
-                                                const int32_t* __restrict__ sel_idx, int nbmax, int hpg, int N,
+                                                const int32_t* __restrict__ sel_idx,
+                                                const int32_t* __restrict__ order, int nbmax, int hpg, int N,
                                                 float scale2, RowMap rm) {
   constexpr int T = 64 * D;
   constexpr int DS = D / 16, DB = D / 32, CH = D / 16;
@@ -537,11 +538,24 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = w & 1, kh = w >> 1;
-  const int h = blockIdx.y;
+  // this workgroup's (head, pair): from the launch order if one is given, else head blockIdx.y
+  // and the pairs of a head in xcd_atom order
+  const int npairs = N >> 7;
+  int h, pidx;
+  if (order) {
+    const int item = order[blockIdx.y * gridDim.x + blockIdx.x];
+    h = item / npairs;
+    pidx = item - h * npairs;
+  } else {
+    h = blockIdx.y;
+    pidx = xcd_atom(blockIdx.x, npairs);
+  }
+  h = __builtin_amdgcn_readfirstlane(h);
+  pidx = __builtin_amdgcn_readfirstlane(pidx);
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   int rowA, rowB;
-  pair_atoms(bs, nbmax, sel_count + (int64_t)h * nbmax, sel_idx + (int64_t)h * nbmax * nbmax,
-             xcd_atom(blockIdx.x, N >> 7), reinterpret_cast<uint32_t*>(smem), rowA, rowB);
+  pair_atoms(bs, nbmax, sel_count + (int64_t)h * nbmax, sel_idx + (int64_t)h * nbmax * nbmax, pidx,
+             reinterpret_cast<uint32_t*>(smem), rowA, rowB);
   const int qa = block_of_row(bs, nbmax, rowA), qb = block_of_row(bs, nbmax, rowB);
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
@@ -1067,18 +1081,18 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 
 prism_status launch_mfma_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                              const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
-                             const RowMap& out, hipStream_t st) {
+                             const int32_t* order, const RowMap& out, hipStream_t st) {
   dim3 grid((unsigned)(g.N / 128), g.heads);  // one workgroup per pair of atoms
   const float scale2 = sm_scale * kLog2e;
   KernelTrace tr("k_fwd", st);
   if (g.d == 64)
     hipLaunchKernelGGL(k_fwd<64>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
-                       (int)g.N, scale2, out);
+                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, order, g.nbmax,
+                       g.hpg, (int)g.N, scale2, out);
   else
     hipLaunchKernelGGL(k_fwd<128>, grid, dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, g.nbmax, g.hpg,
-                       (int)g.N, scale2, out);
+                       (const uint16_t*)v, (uint16_t*)o, (uint16_t*)o_lo, lse, bs, cnt, idx, order, g.nbmax,
+                       g.hpg, (int)g.N, scale2, out);
   return check_launch("k_fwd");
 }
 

@@ -150,9 +150,11 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
                            double p, int32_t* sel_count, int32_t* sel_idx, hipStream_t st);
 // out: where o, o_lo (forward) and dq, dk, dv (backward) go; o_in: where the backward reads o,
 // o_lo.  dout and everything else stay in block order.
+// ws: NULL or bsa_fwd_workspace_bytes(g) bytes of scratch (the launch order of the forward).
+size_t bsa_fwd_workspace_bytes(const Geom& g);
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
-                            const void* v, void* o, void* o_lo, float* lse, const RowMap& out,
+                            const void* v, void* o, void* o_lo, float* lse, void* ws, const RowMap& out,
                             hipStream_t st);
 size_t bsa_bwd_workspace_bytes(const Geom& g);
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,

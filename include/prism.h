@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 1
+#define PRISM_ABI_VERSION 2
 
 typedef enum {
   PRISM_OK = 0,
@@ -185,11 +185,17 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
  *       rounding residual of O, o_lo = rnd(O_fp32 - o), so that o + o_lo carries about 16
  *       significant bits.  prism_bsa_bwd uses it to form delta = dO . O without the bf16
  *       rounding of o, which otherwise dominates the gradient error when the softmax is
- *       peaked (dP - delta cancels). */
+ *       peaked (dP - delta cancels).
+ * workspace: NULL, or device scratch of at least prism_bsa_fwd_workspace_bytes(pb) bytes,
+ *       256-byte aligned, contents on entry irrelevant (workspace_bytes is ignored when NULL).
+ *       With it, the workgroups whose query blocks have the longest lists are launched
+ *       first (the order is built on the device), which shortens the end of the launch;
+ *       the results are the same with or without it. */
+size_t prism_bsa_fwd_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
                            const void* q, const void* k, const void* v, void* o, void* o_lo,
-                           float* lse, void* stream);
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- a7: block-sparse attention backward -------------------------------------------- *
  * Gradient of prism_bsa_fwd with the selection held constant: delta_r = dO_r . O_r,
@@ -219,7 +225,7 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
  * their block-order buffers) are not needed.  Results are bitwise those of the block-order
  * calls followed by prism_permute(inverse = 1).
  * prism_bsa_fwd_tok: q, k, v block order (as for prism_bsa_fwd); o and o_lo out in token order;
- *   lse out [heads, N] in block order.
+ *   lse out [heads, N] in block order; workspace as for prism_bsa_fwd.
  * prism_bsa_bwd_tok: q, k, v block order; o, o_lo (prism_bsa_fwd_tok's outputs) and dout in
  *   token order; lse block order; dq, dk, dv out [N, heads, head_dim] fp32 in token order.
  *   The workspace (prism_bsa_bwd_tok_workspace_bytes, 256-byte aligned) also holds a
@@ -228,7 +234,7 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
 prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
                                const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
                                const void* q, const void* k, const void* v, void* o, void* o_lo,
-                               float* lse, void* stream);
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 size_t prism_bsa_bwd_tok_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_bwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,
                                const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,

@@ -17,10 +17,10 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
-    assert P.prism_abi_version() == 1
+    assert P.prism_abi_version() == 2
 
 
 def test_shape_table_matches_oracle_enumeration():
@@ -61,9 +61,28 @@ def test_null_and_alignment_rejected(L):
     assert L.prism_zone_stats(ctypes.byref(pb), MISALIGNED, None, 1e-6, FAKE, FAKE, None, None) == 5
     # audio given but no zone_audio output
     assert L.prism_zone_stats(ctypes.byref(pb), FAKE, FAKE, 1e-6, FAKE, FAKE, None, None) == 1
-    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, None, FAKE, None, FAKE, None) == 1
+    assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, None, FAKE, None, FAKE, None, 0,
+                           None) == 1
     assert L.prism_bsa_fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE,
-                           None) == 5
+                           None, 0, None) == 5
+
+
+def test_forward_workspace(L):
+    """The forward's workspace is optional (NULL: plain launch order); when given it must be
+    256-byte aligned and at least prism_bsa_fwd_workspace_bytes large (launch order and work
+    estimates, one int32 each per pair of 64-row atoms and head)."""
+    pb = _pb()
+    need = P.prism_bsa_fwd_workspace_bytes(pb)
+    N, heads = 8 * 16 * 16, 2
+    assert need >= 2 * heads * (N // 128) * 4
+    args = [ctypes.byref(pb)] + [FAKE] * 3 + [0.125] + [FAKE] * 4 + [None, FAKE]
+    assert L.prism_bsa_fwd(*args, FAKE, need - 1, None) == 6
+    assert L.prism_bsa_fwd(*args, MISALIGNED, need, None) == 5
+    tok = [ctypes.byref(pb)] + [FAKE] * 4 + [0.125] + [FAKE] * 4 + [None, FAKE]
+    assert L.prism_bsa_fwd_tok(*tok, FAKE, need - 1, None) == 6
+    assert P.prism_bsa_fwd_workspace_bytes(_pb(T=3)) == 0
+    # fp32 problems run the plain kernels and need none
+    assert P.prism_bsa_fwd_workspace_bytes(_pb(dtype=P.F32)) == 0
 
 
 def test_scalar_ranges_rejected(L):
@@ -122,9 +141,10 @@ def test_token_order_attention_validation(L):
     pb = _pb()
     fwd = L.prism_bsa_fwd_tok
     # shape_idx is required: the output rows' tokens come from it
-    assert fwd(ctypes.byref(pb), None, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 1
-    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == 3
-    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, MISALIGNED, None, FAKE, None) == 5
+    assert fwd(ctypes.byref(pb), None, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == 1
+    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == 3
+    assert fwd(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, FAKE, FAKE, MISALIGNED, None, FAKE, None, 0,
+               None) == 5
     need = P.prism_bsa_bwd_tok_workspace_bytes(pb)
     N, d = 8 * 16 * 16, 64
     # the block-order workspace plus a bf16 block-order copy of dO

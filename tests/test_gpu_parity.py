@@ -191,6 +191,32 @@ def test_empty_lists(run):
             assert_close_attn(name + " (empty lists)", f64(mine), oracle.unpermute(ref, o["pos"], c.heads))
 
 
+def test_forward_launch_order_bitwise(run):
+    """The forward's launch order (built in its optional workspace: pairs with the longest
+    lists first) only changes which workgroup runs when: O and LSE are bitwise those of the
+    plain launch order."""
+    c = run.cfg
+    if c.dtype != "bf16":
+        pytest.skip("fp32 problems run the plain kernels, without a launch order")
+    run.inject_oracle_plan()
+    L = run.layer
+    from dynamic_block_sparse_var_amd import prism_permute
+
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    run.inject_oracle_mask()
+    assert L.fwd_workspace is not None
+    L.attend(c.sm_scale)
+    torch.cuda.synchronize()
+    o1, l1 = L.o.clone(), L.lse.clone()
+    ws, L.fwd_workspace = L.fwd_workspace, None
+    try:
+        L.attend(c.sm_scale)
+        torch.cuda.synchronize()
+    finally:
+        L.fwd_workspace = ws
+    assert torch.equal(o1, L.o) and torch.equal(l1, L.lse)
+
+
 def test_deterministic(run):
     _gpu_attention(run)
     L = run.layer
