@@ -12,7 +12,8 @@
 // (32*(w>>1)..), and the two waves that share the atom rows combine their partial results once
 // at the end.  Atoms are assigned so that each of the 8 XCDs walks a contiguous range of atoms
 // (neighbouring blocks tend to select the same key blocks, which may then still be in that
-// XCD's L2).
+// XCD's L2); a launch order built by attn.hip moves the units with the longest walks to the
+// front of that sequence, so that none of them starts near the end of the launch.
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16): operand A holds A[m = lane%32][8 k-values],
 // operand B holds B[8 k-values][n = lane%32]; both use lane/32 to pick which half of the 16
