@@ -272,8 +272,8 @@ def main():
         write_traffic(args.traffic_from, args.copy_probe_mb or 4096, args.config)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU sharding of this path is "
-              f"described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is built and measured on one "
+              f"GPU; sharding it by head group over several GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
