@@ -8,7 +8,8 @@ runs in the library's kernels; torch only provides memory and streams.  There is
 fallback: if ``libprism.so`` has not been built, loading raises.
 
 :class:`PrismLayer` strings the calls together for one layer (allocating the outputs with
-torch), and :class:`PrismAttentionFunction` wraps forward and backward for autograd.
+torch, once), :class:`PrismAttentionFunction` wraps forward and backward for autograd and
+:class:`PrismAttention` is a module that owns one layer's buffers.
 """
 from __future__ import annotations
 
@@ -278,6 +279,7 @@ class PrismLayer:
         (prism_bsa_fwd_tok / prism_bsa_bwd_tok), with no block-order O, dO or gradient buffers."""
         self.pb = pb
         self.token_io = token_io
+        self.generation = 0  # forwards run through PrismAttentionFunction
         dt = pb.torch_dtype
         N, H_, d, G, Z, NB = pb.N, pb.heads, pb.head_dim, pb.groups, pb.Z, pb.nbmax
         e = dict(device=device)
@@ -378,20 +380,42 @@ class PrismLayer:
 
 
 class PrismAttentionFunction(torch.autograd.Function):
-    """Autograd wrapper: (q, k, v) token order [N, heads, d] -> o.  The selection is a
-    constant of the backward (no gradient to statistics, shapes, pooling or selection)."""
+    """Autograd wrapper: (q, k, v) token order [N, heads, d] -> o, computed by a caller-owned
+    :class:`PrismLayer` (built with backward=True, token_io=True), whose buffers are reused from
+    call to call.  The selection is a constant of the backward (no gradient to statistics,
+    shapes, pooling or selection).  One forward per backward: the layer keeps the state of its
+    last forward, so a second forward on the same layer before the first one's backward makes
+    that backward raise."""
 
     @staticmethod
-    def forward(ctx, q, k, v, a, pb, sm_scale, k_abs, k_frac, p):
-        layer = PrismLayer(pb, device=q.device, backward=True, token_io=True)
+    def forward(ctx, q, k, v, a, layer, sm_scale, k_abs, k_frac, p):
         o = layer.forward(q.contiguous(), k.contiguous(), v.contiguous(), a, sm_scale, k_abs, k_frac, p)
-        ctx.layer, ctx.sm_scale = layer, sm_scale
+        layer.generation += 1
+        ctx.layer, ctx.generation, ctx.sm_scale = layer, layer.generation, sm_scale
         return o.clone()
 
     @staticmethod
     def backward(ctx, do):
+        if ctx.layer.generation != ctx.generation:
+            raise RuntimeError("PrismAttentionFunction: the layer ran another forward before this backward")
         dq, dk, dv = ctx.layer.backward(do.contiguous(), ctx.sm_scale)
         return dq.clone(), dk.clone(), dv.clone(), None, None, None, None, None, None
+
+
+class PrismAttention(torch.nn.Module):
+    """One attention layer for autograd: owns its PrismLayer (allocated once, here) and calls
+    PrismAttentionFunction with the layer's knobs (bsa_sparsity s maps to k_frac = 1 - s,
+    bsa_cdf_threshold to p)."""
+
+    def __init__(self, pb: Problem, sm_scale: float, k_abs: int = 0, k_frac: float = 0.05, p: float = 0.9,
+                 device="cuda"):
+        super().__init__()
+        self.layer = PrismLayer(pb, device=device, backward=True, token_io=True)
+        self.sm_scale, self.k_abs, self.k_frac, self.p = float(sm_scale), int(k_abs), float(k_frac), float(p)
+
+    def forward(self, q, k, v, a=None):
+        return PrismAttentionFunction.apply(q, k, v, a, self.layer, self.sm_scale, self.k_abs, self.k_frac,
+                                            self.p)
 
 
 def default_sm_scale(head_dim: int) -> float:

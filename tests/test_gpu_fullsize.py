@@ -4,9 +4,16 @@ case), in the launch configuration the benchmark times.
 Zone statistics, shapes and the complete selection are compared against the oracle over
 every zone and every query block.  Attention outputs and gradients, given the oracle's
 shapes and mask, are compared on sampled blocks the oracle computes one by one: O, LSE and
-dQ on random query blocks of every head, dK and dV on random key blocks of every head drawn
-from those selected by at most 24 query blocks (the oracle's cost of a key block's gradient
-grows with the number of query blocks that attend to it).
+dQ on random query blocks of every head (the C oracle), dK and dV on chosen key blocks of
+every head (the fp64 matrix-product oracle, oracle/attn_rows.py, whose cost grows with the
+number of query blocks that selected the key block):
+
+* 1080p and 2K: one rarely selected key block (at most 24 selecting query blocks), the key
+  block at the median selector count, and one of the heavy key blocks that the backward's
+  launch order moves to the front (selected by more than 2.5 times the mean; the least
+  selected of them, 2K every head, 1080p the first head);
+* 2K stress: the least selected key block of every head (every key block there is chosen by
+  hundreds of query blocks of 256 rows, which is the dispersed regime Top-p expands).
 """
 import numpy as np
 import pytest
@@ -14,13 +21,14 @@ import torch
 
 import oracle
 import synth
-from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, compare_shapes, f64, say)
+from oracle import attn_rows
+from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, compare_shapes, f64, report, say)
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["720p", "1080p", "2k", "2k_stress"]
 QB_PER_HEAD = 3
-KB_PER_HEAD = 1
+HEAVY = 2.5  # the backward launch order's threshold for dK/dV work (times the mean per atom)
 
 
 @pytest.fixture(scope="module", params=FULL)
@@ -45,8 +53,8 @@ def test_plan_full(run):
     np.testing.assert_allclose(za[:, 1:], o["stats"]["vhat"], rtol=1e-4, atol=1e-6)
     hard, soft, n = compare_shapes(L.shape_idx.cpu().numpy(), o["stats"], o["shapes"], c.tau128, c.tau256)
     vols = np.array([64] * 7 + [128] * 6 + [256] * 3)[o["shapes"]["shape_idx"]]
-    say(f"  {c.name}: {n} zones, B=64/128/256: {(vols == 64).sum()}/{(vols == 128).sum()}/{(vols == 256).sum()}, "
-        f"hard {hard}, near-tie {soft}")
+    report(f"{c.name} shapes: {n} zones, B=64/128/256: {(vols == 64).sum()}/{(vols == 128).sum()}/"
+           f"{(vols == 256).sum()}, hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(n)
 
 
@@ -58,36 +66,57 @@ def test_select_full(run):
     np.testing.assert_allclose(f64(L.qbar), o["qbar"], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(f64(L.kbar), o["kbar"], rtol=1e-5, atol=1e-5)
     hard, soft, rows = compare_masks(L.sel_count.cpu().numpy(), L.sel_idx.cpu().numpy(), o["sel_count"],
-                                     o["sel_idx"], o["sel_info"], o["nblocks"], c.groups)
+                                     o["sel_idx"], o["sel_info"], o["nblocks"], c.groups, qbar=o["qbar"],
+                                     kbar=o["kbar"], sm_scale=c.sm_scale)
     nb = int(o["nblocks"][0])
     frac = (o["sel_count"][:, :nb] / nb).mean()
-    say(f"  {c.name}: {rows} rows, mean selected block fraction {frac:.3f}, hard {hard}, near-tie {soft}")
+    report(f"{c.name} masks: {rows} rows, mean selected block fraction {frac:.3f}, hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(rows)
 
 
+def key_block_picks(c, o, rng):
+    """{head: [(label, key block)]} for the dK/dV checks (see the module docstring)."""
+    nb = int(o["nblocks"][0])
+    bs = o["block_start"][0]
+    atoms = np.diff(bs)[:nb] // 64
+    picks = {}
+    for h in range(c.heads):
+        col = attn_rows.selector_counts(o["sel_count"], o["sel_idx"], nb, h)
+        used = np.flatnonzero(col > 0)
+        order = used[np.argsort(col[used], kind="stable")]
+        if c.name == "2k_stress":
+            picks[h] = [("least selected", int(order[0]))]
+            continue
+        out = []
+        rare = np.flatnonzero((col > 0) & (col <= 24))
+        if len(rare):
+            out.append(("rare", int(rng.choice(rare))))
+        out.append(("median", int(order[len(order) // 2])))
+        if h == 0 or c.name == "2k":
+            mean_atom = (col * atoms).sum() / atoms.sum()
+            heavy = order[col[order] > HEAVY * mean_atom]
+            out.append(("heavy", int(heavy[0]) if len(heavy) else int(order[-1])))
+        picks[h] = out
+    return picks, col
+
+
+@pytest.mark.timeout(1500)
 def test_attention_full_sampled(run):
     c, o = run.cfg, run.orc
     rng = np.random.default_rng(c.seed)
     nb = int(o["nblocks"][0])
     qmask = np.zeros((c.heads, c.nbmax), np.uint8)
-    kmask = np.zeros((c.heads, c.nbmax), np.uint8)
-    colcount = np.zeros((c.heads, nb), np.int64)
     for h in range(c.heads):
         qmask[h, rng.choice(nb, QB_PER_HEAD, replace=False)] = 1
-        for i in range(nb):
-            colcount[h, o["sel_idx"][h, i, :o["sel_count"][h, i]]] += 1
-        cand = np.flatnonzero((colcount[h] > 0) & (colcount[h] <= 24))
-        if len(cand):
-            kmask[h, rng.choice(cand, min(KB_PER_HEAD, len(cand)), replace=False)] = 1
-    say(f"  {c.name}: oracle attention on {int(qmask.sum())} query blocks, {int(kmask.sum())} key blocks")
+    say(f"  {c.name}: oracle attention on {int(qmask.sum())} query blocks")
     vp = oracle.permute(run.inp["v"], o["pos"], c.heads)
     of, lf = oracle.attn_fwd(o["qp"], o["kp"], vp, o["block_start"], o["nblocks"], c.groups, o["sel_count"],
                              o["sel_idx"], c.sm_scale, qblock_mask=qmask)
-    ob = None
+    ob = dop = None
     if run.backward:
         dop = oracle.permute(run.inp["dout"], o["pos"], c.heads)
         ob = oracle.attn_bwd(o["qp"], o["kp"], vp, dop, o["block_start"], o["nblocks"], c.groups, o["sel_count"],
-                             o["sel_idx"], c.sm_scale, qblock_mask=qmask, kblock_mask=kmask)
+                             o["sel_idx"], c.sm_scale, qblock_mask=qmask, kblock_mask=np.zeros_like(qmask))
     # GPU, given the oracle's plan and mask, in block order
     run.inject_oracle_plan()
     L = run.layer
@@ -115,23 +144,33 @@ def test_attention_full_sampled(run):
     dl = np.abs(pick(L.lse.cpu().numpy().astype(np.float64), qrows) - pick(lf, qrows)).max()
     say(f"  LSE: max_abs={dl:.3e}")
     assert dl <= LSE_ABS
-    if run.backward:
-        assert_close_attn("dQ (sampled query blocks)", pick(f64(L.dqp), qrows), pick(ob["dq"], qrows))
-        krows = rows_of(kmask)
-        if krows:
-            assert_close_attn("dK (sampled key blocks)", pick(f64(L.dkp), krows), pick(ob["dk"], krows))
-            assert_close_attn("dV (sampled key blocks)", pick(f64(L.dvp), krows), pick(ob["dv"], krows))
-        # exact identities over all keys of a head, at any size: every softmax row sums to 1,
-        # so sum_c dV_c = sum_r dO_r; and every row of dS sums to 0, so sum_c dK_c = 0
-        dop = oracle.permute(run.inp["dout"], o["pos"], c.heads).astype(np.float64)
-        for h in range(c.heads):
-            dv = L.dvp[h].double().sum(0).cpu().numpy()
-            ref = dop[h].sum(0)
-            rel = np.abs(dv - ref).max() / max(np.abs(ref).max(), 1e-30)
-            dk_sum = L.dkp[h].double().sum(0).abs().max().item()
-            dk_scale = L.dkp[h].double().abs().sum(0).max().item()
-            say(f"  head {h}: |sum dV - sum dO| rel {rel:.2e}; |sum dK| / sum |dK| {dk_sum / dk_scale:.2e}")
-            assert rel < 1e-4 and dk_sum <= 1e-4 * dk_scale
+    if not run.backward:
+        return
+    assert_close_attn("dQ (sampled query blocks)", pick(f64(L.dqp), qrows), pick(ob["dq"], qrows))
+    # dK, dV of the chosen key blocks, element by element
+    picks, _ = key_block_picks(c, o, rng)
+    assert sum(len(v) for v in picks.values()) >= c.heads, "no key block sampled"
+    dkp, dvp = L.dkp.cpu().numpy(), L.dvp.cpu().numpy()
+    for h, lst in picks.items():
+        head = attn_rows.Head(o["qp"], o["kp"], vp, dop, bs, nb, o["sel_count"], o["sel_idx"], h, c.sm_scale)
+        for label, j in lst:
+            sel = head.selectors(j)
+            say(f"  head {h} key block {j} ({label}, {bs[j + 1] - bs[j]} rows, {len(sel)} selecting query "
+                f"blocks): oracle ...")
+            rows, dk, dv = head.dkdv(j, sel)
+            assert_close_attn(f"dK h{h} kb{j} ({label})", dkp[h, rows].astype(np.float64), dk)
+            assert_close_attn(f"dV h{h} kb{j} ({label})", dvp[h, rows].astype(np.float64), dv)
+        del head
+    # exact identities over all keys of a head, at any size: every softmax row sums to 1,
+    # so sum_c dV_c = sum_r dO_r; and every row of dS sums to 0, so sum_c dK_c = 0
+    for h in range(c.heads):
+        dv = L.dvp[h].double().sum(0).cpu().numpy()
+        ref = dop[h].astype(np.float64).sum(0)
+        rel = np.abs(dv - ref).max() / max(np.abs(ref).max(), 1e-30)
+        dk_sum = L.dkp[h].double().sum(0).abs().max().item()
+        dk_scale = L.dkp[h].double().abs().sum(0).max().item()
+        say(f"  head {h}: |sum dV - sum dO| rel {rel:.2e}; |sum dK| / sum |dK| {dk_sum / dk_scale:.2e}")
+        assert rel < 1e-4 and dk_sum <= 1e-4 * dk_scale
 
 
 def test_token_order_path_full(run):

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from dynamic_block_sparse_var_amd import PrismLayer
-from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, compare_shapes, f64, say)
+from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, compare_shapes, f64, report, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,11 @@ SMALL = {
                                backward=True, seed=2002),
     "d64_groups2": synth.Config("d64_groups2", 8, 16, 32, 4, 64, "bf16", blobs=1, k_abs=3, k_frac=0.0, p=0.8,
                                 backward=True, seed=2003, groups=2, gamma=6.0),
+    # the 2K stress regime's generator on a grid the oracle covers in full: field amplitude 0.1
+    # on V (near-isotropic zones, 256-row blocks), logits x 0.3, k 2 %, p 0.95, so Top-p
+    # expands most lists far beyond k (the pages' dispersed-attention case)
+    "stress_small": synth.Config("stress_small", 16, 16, 32, 2, 128, "bf16", blobs=2, k_abs=0, k_frac=0.02,
+                                 p=0.95, backward=True, seed=2004, amp_v=0.1, gamma=16.0 * 0.3),
 }
 
 
@@ -50,7 +55,7 @@ def test_zone_stats_and_shapes(run):
     np.testing.assert_allclose(za[:, 1:], o["stats"]["vhat"], rtol=1e-4, atol=1e-6)
     shape = L.shape_idx.cpu().numpy()
     hard, soft, n = compare_shapes(shape, o["stats"], o["shapes"], c.tau128, c.tau256)
-    say(f"  shapes: {n} zones, hard mismatches {hard}, near-tie mismatches {soft}")
+    report(f"{c.name} shapes: {n} zones, hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(n)
     if soft == 0:
         assert np.array_equal(L.zone_block_off.cpu().numpy(), o["shapes"]["zone_block_off"])
@@ -93,8 +98,9 @@ def test_select(run):
     run.gpu_select()
     L, o, c = run.layer, run.orc, run.cfg
     hard, soft, rows = compare_masks(L.sel_count.cpu().numpy(), L.sel_idx.cpu().numpy(), o["sel_count"],
-                                     o["sel_idx"], o["sel_info"], o["nblocks"], c.groups)
-    say(f"  masks: {rows} rows, hard mismatches {hard}, near-tie mismatches {soft}")
+                                     o["sel_idx"], o["sel_info"], o["nblocks"], c.groups, qbar=o["qbar"],
+                                     kbar=o["kbar"], sm_scale=c.sm_scale)
+    report(f"{c.name} masks: {rows} rows, hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(rows)
     nb = o["nblocks"]
     hpg = c.heads // c.groups
@@ -255,6 +261,43 @@ def test_all_blocks_is_dense_attention(run):
     assert_close_attn("dense O", f64(L.o), ref.permute(1, 0, 2).double().numpy())
 
 
+def test_all_blocks_dense_backward(run):
+    """Every key block selected (the dense baseline's selection): the sparse backward must equal
+    the gradient of dense softmax attention, taken by torch autograd in fp64 on the CPU from the
+    same inputs (per head: O = softmax(sm_scale Q K^T) V, loss = sum O * dO)."""
+    if not run.backward:
+        pytest.skip("forward-only config")
+    c, o = run.cfg, run.orc
+    run.inject_oracle_plan()
+    L = run.layer
+    from dynamic_block_sparse_var_amd import prism_permute
+
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    nb = o["nblocks"]
+    hpg = c.heads // c.groups
+    cnt = np.zeros_like(o["sel_count"])
+    idx = np.zeros_like(o["sel_idx"])
+    for h in range(c.heads):
+        n = nb[h // hpg]
+        cnt[h, :n] = n
+        idx[h, :n, :n] = np.arange(n)
+    L.sel_count.copy_(torch.from_numpy(cnt))
+    L.sel_idx.copy_(torch.from_numpy(idx))
+    L.attend(c.sm_scale)
+    L.backward(run.dout, c.sm_scale)
+    torch.cuda.synchronize()
+    ref = {name: np.zeros((c.N, c.heads, c.d)) for name in ("dq", "dk", "dv")}
+    for h in range(c.heads):
+        q, k, v = (torch.from_numpy(run.inp[x][:, h, :]).double().requires_grad_() for x in ("q", "k", "v"))
+        out = torch.softmax((q @ k.T) * c.sm_scale, dim=-1) @ v
+        out.backward(torch.from_numpy(run.inp["dout"][:, h, :]).double())
+        for name, t in (("dq", q), ("dk", k), ("dv", v)):
+            ref[name][:, h, :] = t.grad.numpy()
+        del q, k, v, out
+    for name in ("dq", "dk", "dv"):
+        assert_close_attn(f"dense {name}", f64(getattr(L, name)), ref[name])
+
+
 def test_fixed_shapes_path(run):
     """Fixed 4x4x4 blocks for every zone (the pages' fixed-block ablation): layout exact against
     the oracle's block order for the same shape map, then permute, pool, selection and the
@@ -282,8 +325,8 @@ def test_fixed_shapes_path(run):
     np.testing.assert_allclose(f64(L.qbar), qbar, rtol=1e-5, atol=1e-5)
     cnt, idx, info = oracle.select(qbar, kbar, nb, c.groups, c.sm_scale, c.k_abs, c.k_frac, c.p)
     hard, soft, rows = compare_masks(L.sel_count.cpu().numpy(), L.sel_idx.cpu().numpy(), cnt, idx, info, nb,
-                                     c.groups)
-    say(f"  fixed 4x4x4: {int(nb[0])} blocks, {rows} rows, hard {hard}, near-tie {soft}")
+                                     c.groups, qbar=qbar, kbar=kbar, sm_scale=c.sm_scale)
+    report(f"{c.name} fixed 4x4x4 masks: {int(nb[0])} blocks, {rows} rows, hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(rows)
     L.sel_count.copy_(torch.from_numpy(cnt))
     L.sel_idx.copy_(torch.from_numpy(idx))

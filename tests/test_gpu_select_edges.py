@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from dynamic_block_sparse_var_amd import BF16, make_problem, prism_select_blocks
-from parity_util import NEAR_TIE, cap, compare_masks, say
+from parity_util import NEAR_TIE, cap, compare_masks, report, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,12 @@ def _oracle_select(qbar, kbar, nb, sm_scale, k_abs, k_frac, p, rows=None):
                          nb, 1, sm_scale, k_abs, k_frac, p, row_mask=rows)
 
 
+def _scores(qbar, kbar, sm):
+    """compare_masks arguments for the cut check: the pooled values as the oracle saw them."""
+    return dict(qbar=qbar.astype(np.float32).astype(np.float64), kbar=kbar.astype(np.float32).astype(np.float64),
+                sm_scale=sm)
+
+
 def _pooled(rng, heads, nbmax, nb, d, scale=1.0):
     x = np.zeros((heads, nbmax, d), np.float32)
     x[:, :nb] = (scale * rng.standard_normal((heads, nb, d))).astype(np.float32)
@@ -73,9 +79,9 @@ def test_random_scores(k_abs, k_frac, p):
     sm = 3.0 / math.sqrt(d)
     gc, gi = _gpu_select(T, H, W, heads, d, bs, qbar, kbar, sm, k_abs, k_frac, p)
     oc, oi, info = _oracle_select(qbar, kbar, nb, sm, k_abs, k_frac, p)
-    hard, soft, rows = compare_masks(gc, gi, oc, oi, info, nb, 1)
-    say(f"  k_abs={k_abs} k_frac={k_frac} p={p}: {rows} rows, mean |S| {oc[:, :nb[0]].mean():.1f}, "
-        f"hard {hard}, near-tie {soft}")
+    hard, soft, rows = compare_masks(gc, gi, oc, oi, info, nb, 1, **_scores(qbar, kbar, sm))
+    report(f"select edges k_abs={k_abs} k_frac={k_frac} p={p}: {rows} rows, mean |S| {oc[:, :nb[0]].mean():.1f}, "
+           f"hard {hard}, near-tie {soft}")
     assert hard == 0 and soft <= cap(rows)
     assert (gc[:, nb[0]:] == 0).all()
 
@@ -178,8 +184,9 @@ def test_maximum_block_count_sampled_rows():
     rows[0, [0, n - 1]] = 1
     gc, gi = _gpu_select(T, H, W, heads, d, bs, qbar, kbar, sm, 0, 0.05, 0.9)
     oc, oi, info = _oracle_select(qbar, kbar, nb, sm, 0, 0.05, 0.9, rows=rows)
-    hard, soft, nrows = compare_masks(gc, gi, oc, oi, info, nb, 1, rows_mask=rows)
-    say(f"  8192 blocks: {nrows} rows, mean |S| {oc[0][rows[0] == 1].mean():.1f}, hard {hard}, near-tie {soft}")
+    hard, soft, nrows = compare_masks(gc, gi, oc, oi, info, nb, 1, rows_mask=rows, **_scores(qbar, kbar, sm))
+    report(f"select edges 8192 blocks: {nrows} rows, mean |S| {oc[0][rows[0] == 1].mean():.1f}, hard {hard}, "
+           f"near-tie {soft}")
     assert hard == 0 and soft <= cap(nrows)
 
 
@@ -194,5 +201,5 @@ def test_two_blocks():
     for k_abs, p in ((1, 0.0), (1, 0.999), (2, 0.0), (1, 0.3)):
         gc, gi = _gpu_select(8, 8, 8, heads, d, bs, qbar, kbar, 0.5, k_abs, 0.0, p)
         oc, oi, info = _oracle_select(qbar, kbar, nb, 0.5, k_abs, 0.0, p)
-        hard, soft, rows = compare_masks(gc, gi, oc, oi, info, nb, 1)
+        hard, soft, rows = compare_masks(gc, gi, oc, oi, info, nb, 1, **_scores(qbar, kbar, 0.5))
         assert hard == 0 and soft == 0, (k_abs, p)

@@ -560,3 +560,75 @@ def test_attention_backward_matches_autograd_and_finite_differences():
             step = (plus[name][hh, n, e] - minus[name][hh, n, e])
             fd = (loss(plus["q"], plus["k"], plus["v"]) - loss(minus["q"], minus["k"], minus["v"])) / step
             assert fd == pytest.approx(grad[hh, n, e], rel=2e-3, abs=2e-5)
+
+
+# ------------------------------------------------ attention by whole-block products (attn_rows)
+
+
+def test_attn_rows_matches_autograd_of_masked_dense():
+    """oracle/attn_rows.py (the matrix-product form used for large key blocks) against torch
+    autograd of dense attention under the token mask of the block lists (fp64): O, LSE, dQ of
+    every query block and dK, dV of every key block."""
+    import torch
+
+    from oracle import attn_rows
+
+    cfg = synth.CONFIGS["tiny"].replace(gamma=4.0)
+    inp = synth.make_inputs(cfg, with_dout=True)
+    r = oracle.forward_path(inp)
+    vp = oracle.permute(inp["v"], r["pos"], cfg.heads)
+    dop = oracle.permute(inp["dout"], r["pos"], cfg.heads)
+    mask, _ = _token_mask(r, cfg.heads, cfg.N)
+    q, k, v = (torch.tensor(np.asarray(x, np.float64), requires_grad=True) for x in (r["qp"], r["kp"], vp))
+    s = torch.einsum("hnd,hmd->hnm", q, k) * cfg.sm_scale
+    s = s.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    lse = torch.logsumexp(s, -1)
+    o = torch.softmax(s, -1) @ v
+    o.backward(torch.from_numpy(np.asarray(dop, np.float64)))
+    bs, nb = r["block_start"][0], int(r["nblocks"][0])
+    for h in range(cfg.heads):
+        H = attn_rows.Head(r["qp"], r["kp"], vp, dop, bs, nb, r["sel_count"], r["sel_idx"], h, cfg.sm_scale)
+        for i in range(nb):
+            rows, oi, li = H.fwd(i)
+            np.testing.assert_allclose(oi, o.detach().numpy()[h, rows], rtol=1e-10, atol=1e-10)
+            np.testing.assert_allclose(li, lse.detach().numpy()[h, rows], rtol=1e-12, atol=1e-10)
+            rows, dq = H.dq(i)
+            np.testing.assert_allclose(dq, q.grad.numpy()[h, rows], rtol=1e-9, atol=1e-9)
+        for j in range(nb):
+            rows, dk, dv = H.dkdv(j)
+            np.testing.assert_allclose(dk, k.grad.numpy()[h, rows], rtol=1e-9, atol=1e-9)
+            np.testing.assert_allclose(dv, v.grad.numpy()[h, rows], rtol=1e-9, atol=1e-9)
+
+
+def test_attn_rows_matches_c_oracle_on_mixed_volumes():
+    """The matrix-product form against the C oracle's per-row loops on a bf16-exact layout with
+    64-, 128- and 256-row blocks and Top-p-extended lists, on sampled query and key blocks."""
+    from oracle import attn_rows
+
+    cfg = synth.Config("mixed", 8, 16, 32, 2, 64, "bf16", blobs=1, k_abs=0, k_frac=0.1, p=0.9, backward=True,
+                       seed=3101, gamma=8.0)
+    inp = synth.make_inputs(cfg, with_dout=True)
+    r = oracle.forward_path(inp)
+    vols = np.array([64] * 7 + [128] * 6 + [256] * 3)[r["shapes"]["shape_idx"]]
+    assert len(np.unique(vols)) >= 2
+    vp = oracle.permute(inp["v"], r["pos"], cfg.heads)
+    dop = oracle.permute(inp["dout"], r["pos"], cfg.heads)
+    g = oracle.attn_bwd(r["qp"], r["kp"], vp, dop, r["block_start"], r["nblocks"], 1, r["sel_count"],
+                        r["sel_idx"], cfg.sm_scale)
+    of, lf = oracle.attn_fwd(r["qp"], r["kp"], vp, r["block_start"], r["nblocks"], 1, r["sel_count"], r["sel_idx"],
+                             cfg.sm_scale)
+    bs, nb = r["block_start"][0], int(r["nblocks"][0])
+    for h in range(cfg.heads):
+        H = attn_rows.Head(r["qp"], r["kp"], vp, dop, bs, nb, r["sel_count"], r["sel_idx"], h, cfg.sm_scale)
+        col = attn_rows.selector_counts(r["sel_count"], r["sel_idx"], nb, h)
+        for i in range(0, nb, 3):
+            rows, oi, li = H.fwd(i)
+            np.testing.assert_allclose(oi, of[h, rows], rtol=1e-10, atol=1e-10)
+            np.testing.assert_allclose(li, lf[h, rows], rtol=1e-12, atol=1e-10)
+            rows, dq = H.dq(i)
+            np.testing.assert_allclose(dq, g["dq"][h, rows], rtol=1e-9, atol=1e-9)
+        for j in range(0, nb, 3):
+            assert len(H.selectors(j)) == col[j]
+            rows, dk, dv = H.dkdv(j)
+            np.testing.assert_allclose(dk, g["dk"][h, rows], rtol=1e-9, atol=1e-9)
+            np.testing.assert_allclose(dv, g["dv"][h, rows], rtol=1e-9, atol=1e-9)
