@@ -140,10 +140,32 @@ def forward_pair_tiles(layer, pb):
     return union_units, atom_units
 
 
+def host_record():
+    """nproc, the threads this process may use, and the CPU model name."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable_threads": usable, "cpu_model": model}
+
+
 def cpu_baseline(inp, budget_s=20.0):
     """The oracle as it stands, on the same inputs: the planning half (stats, shapes, block
-    layout, permute + pool of Q and K, full selection) timed in full, and the attention on a
-    sample of query blocks, extrapolated by executed query-key pairs."""
+    layout, permute + pool of Q and K, full selection) timed in full; the attention's three
+    passes timed on samples and extrapolated by the query-key pairs each pass visits:
+    the forward on sampled query blocks, the backward's row statistics + dQ on the same
+    blocks, and its row statistics + dK/dV on sampled key blocks (chosen among those few query
+    blocks select, so that their row statistics stay cheap).  The oracle reports the wall time
+    of each of its backward passes, so every pass is timed on its own."""
     import numpy as np
 
     import oracle
@@ -159,39 +181,75 @@ def cpu_baseline(inp, budget_s=20.0):
     bs, nb = orc["block_start"][0], int(orc["nblocks"][0])
     sizes = np.diff(bs)[:nb].astype(np.int64)
     rowpairs = np.zeros((cfg.heads, nb), np.int64)
+    colpairs = np.zeros((cfg.heads, nb), np.int64)      # pairs the dK/dV pass visits per key block
+    selectors = [[[] for _ in range(nb)] for _ in range(cfg.heads)]
     for h in range(cfg.heads):
         for i in range(nb):
-            rowpairs[h, i] = sizes[i] * sizes[orc["sel_idx"][h, i, :orc["sel_count"][h, i]]].sum()
+            lst = orc["sel_idx"][h, i, :orc["sel_count"][h, i]]
+            rowpairs[h, i] = sizes[i] * sizes[lst].sum()
+            colpairs[h, lst] += sizes[i] * sizes[lst]
+            for j in lst:
+                selectors[h][j].append(i)
     total = int(rowpairs.sum())
     rng = np.random.default_rng(0)
     nq = max(1, nth // cfg.heads)
-    spent, t_fwd, t_bwd, pairs_s, rounds = 0.0, 0.0, 0.0, 0, 0
-    while spent < budget_s and rounds < 64:
-        mask = np.zeros((cfg.heads, cfg.nbmax), np.uint8)
+    args = (orc["qp"], orc["kp"], vp, dop, orc["block_start"], orc["nblocks"], 1, orc["sel_count"], orc["sel_idx"],
+            cfg.sm_scale)
+    zero = np.zeros((cfg.heads, cfg.nbmax), np.uint8)
+    t_fwd = t_rs = t_dq = t_dkdv = 0.0
+    pq = pk = prs = 0
+    rq = rk = 0
+    spent = 0.0
+    # query blocks: forward, then row statistics + dQ
+    while spent < 0.6 * budget_s and rq < 64:
+        mask = zero.copy()
         for h in range(cfg.heads):
             mask[h, rng.choice(nb, size=min(nq, nb), replace=False)] = 1
-        pairs_s += int(rowpairs[mask[:, :nb].astype(bool)].sum())
-        t0 = time.perf_counter()
-        oracle.attn_fwd(orc["qp"], orc["kp"], vp, orc["block_start"], orc["nblocks"], 1, orc["sel_count"],
-                        orc["sel_idx"], cfg.sm_scale, qblock_mask=mask, nthreads=nth)
-        t1 = time.perf_counter()
-        oracle.attn_bwd(orc["qp"], orc["kp"], vp, dop, orc["block_start"], orc["nblocks"], 1, orc["sel_count"],
-                        orc["sel_idx"], cfg.sm_scale, qblock_mask=mask,
-                        kblock_mask=np.zeros_like(mask), nthreads=nth)
-        t2 = time.perf_counter()
-        t_fwd += t1 - t0
-        t_bwd += t2 - t1
-        spent += t2 - t0
-        rounds += 1
-    # dK/dV visit the same query-key pairs with the same per-pair arithmetic as the
-    # row statistics + dQ pass, so the backward per pair is taken as twice that pass
-    per_pair = (t_fwd + 2.0 * t_bwd) / max(pairs_s, 1)
-    est_ms = (t_plan + per_pair * total) * 1e3
+        pq += int(rowpairs[mask[:, :nb].astype(bool)].sum())
+        a = time.perf_counter()
+        oracle.attn_fwd(*args[:3], *args[4:], qblock_mask=mask, nthreads=nth)
+        b = time.perf_counter()
+        oracle.attn_bwd(*args, qblock_mask=mask, kblock_mask=zero, nthreads=nth)
+        c = time.perf_counter()
+        ph = oracle.last_bwd_phase_seconds()
+        t_fwd += b - a
+        t_rs += ph[0]
+        t_dq += ph[1]
+        spent += c - a
+        rq += 1
+    # key blocks: row statistics of their selectors + dK/dV
+    few = [np.flatnonzero((np.array([len(x) for x in selectors[h]]) > 0)
+                          & (np.array([len(x) for x in selectors[h]]) <= 24)) for h in range(cfg.heads)]
+    while spent < budget_s and rk < 64:
+        kmask = zero.copy()
+        need = np.zeros((cfg.heads, nb), bool)
+        for h in range(cfg.heads):
+            pool = few[h] if len(few[h]) else np.flatnonzero(colpairs[h] > 0)
+            for j in rng.choice(pool, size=min(nq, len(pool)), replace=False):
+                kmask[h, j] = 1
+                pk += int(colpairs[h, j])
+                need[h, selectors[h][j]] = True
+        prs += int(rowpairs[need].sum())
+        a = time.perf_counter()
+        oracle.attn_bwd(*args, qblock_mask=zero, kblock_mask=kmask, nthreads=nth)
+        ph = oracle.last_bwd_phase_seconds()
+        t_rs += ph[0]
+        t_dkdv += ph[2]
+        spent += time.perf_counter() - a
+        rk += 1
+    fwd_pp = t_fwd / max(pq, 1)
+    rs_pp = t_rs / max(pq + prs, 1)
+    dq_pp = t_dq / max(pq, 1)
+    dkdv_pp = t_dkdv / max(pk, 1)
+    # forward + backward (row statistics, dQ, dK/dV) over every pair
+    est_ms = (t_plan + total * (fwd_pp + rs_pp + dq_pp + dkdv_pp)) * 1e3
     sample = (f"planning (stats, shapes, layout, permute+pool Q/K, full selection) timed in full "
-              f"({t_plan:.1f} s); attention fwd + row-stat/dQ timed on {rounds} x {nq} query blocks per head "
-              f"({pairs_s:,} of {total:,} query-key pairs, {spent:.1f} s), dK/dV taken equal to the dQ pass per "
-              f"pair, extrapolated by pairs")
-    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": nth, "kind": "oracle", "sample": sample}
+              f"({t_plan:.1f} s); forward and row-stat+dQ passes timed on {rq} x {nq} query blocks per head "
+              f"({pq:,} pairs), row-stat+dK/dV pass on {rk} x {nq} key blocks per head ({pk:,} dK/dV pairs, "
+              f"{prs:,} row-stat pairs), {spent:.1f} s in all; per-pair rates (ns): forward {fwd_pp * 1e9:.2f}, "
+              f"row statistics {rs_pp * 1e9:.2f}, dQ {dq_pp * 1e9:.2f}, dK/dV {dkdv_pp * 1e9:.2f}; extrapolated to all {total:,} pairs")
+    return {"value": round(est_ms, 1), "unit": "ms/layer", "cores": nth, "kind": "oracle", "sample": sample,
+            **host_record()}
 
 
 def write_traffic(d, probe_mb, config):
@@ -243,67 +301,26 @@ def write_traffic(d, probe_mb, config):
     print(json.dumps({k: v.get("bytes_per_launch") for k, v in res.items()}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="2k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--copy-probe-mb", type=int, default=0,
-                    help="before timing, run one plain device copy of this many MiB (a known-size reference "
-                         "for hardware byte counters)")
-    ap.add_argument("--block-io", action="store_true",
-                    help="block-order attention calls with separate permutes of O, dO and the gradients")
-    ap.add_argument("--dense", action="store_true",
-                    help="dense baseline: every key block selected (k = N_b) on the same kernels")
-    ap.add_argument("--fixed-shape", action="store_true",
-                    help="fixed-block ablation: 4x4x4 blocks in every zone, zone statistics and shape "
-                         "assignment skipped")
-    ap.add_argument("--traffic-from", default=None, metavar="DIR",
-                    help="no GPU work: read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR/FETCH_SIZE and "
-                         "DIR/WRITE_SIZE (taken with --copy-probe-mb on this source tree) and write "
-                         "profiles/traffic.json")
-    args = ap.parse_args()
-    if args.dense and args.fixed_shape:
-        ap.error("--dense and --fixed-shape are separate variants")
-    if args.traffic_from:
-        write_traffic(args.traffic_from, args.copy_probe_mb or 4096, args.config)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is built and measured on one "
-              f"GPU; sharding it by head group over several GPUs is not built.", file=sys.stderr)
-        sys.exit(2)
+# Matrix-core FLOPs each attention kernel issues per query-key pair, in units of d: the
+# forward's S and its split PV (3 products of 2d FLOP), the dQ kernel's recomputed S and dP
+# plus its split dQ (4), the dK/dV kernel's S, dP, split dV and split dK (6).
+ISSUED_PER_PAIR = {"k_fwd": 6.0, "k_dq": 8.0, "k_dkdv": 12.0}
+# Algorithmic FLOPs per pair (SURVEY convention: F_fwd = 4d per pair, F_bwd = 2.5 F_fwd with the
+# recomputed S among the five backward products): the forward's QK^T and PV; the dK/dV kernel's
+# S, dP, dV and dK; the dQ kernel's dQ product (its S and dP repeat the dK/dV kernel's).
+ALG_PER_PAIR = {"k_fwd": 4.0, "k_dq": 2.0, "k_dkdv": 8.0}
 
-    import torch
 
-    import dynamic_block_sparse_var_amd as P
-    import synth
-
-    cfg = synth.CONFIGS[args.config]
-    log(f"bench: config {cfg.name} grid {cfg.T}x{cfg.H}x{cfg.W} heads {cfg.heads} d {cfg.d}; generating inputs")
-    inp = synth.make_inputs(cfg, with_dout=True)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    q = torch.from_numpy(inp["q"]).to(dt).to(dev)
-    k = torch.from_numpy(inp["k"]).to(dt).to(dev)
-    v = torch.from_numpy(inp["v"]).to(dt).to(dev)
-    do = torch.from_numpy(inp["dout"]).to(dt).to(dev)
-    a = torch.from_numpy(inp["a"]).to(dev)
-    pb = P.make_problem(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.groups, cfg.dtype)
-    L = P.PrismLayer(pb, device=dev, backward=True, token_io=not args.block_io)
-    pb32 = P.Problem(pb.T, pb.H, pb.W, pb.heads, pb.head_dim, pb.groups, P.F32)
+def make_step(P, pb, L, cfg, q, k, v, a, do, block_io, fixed, k_abs, k_frac):
+    """One layer, forward + backward, as a function of an optional list of events to mark the
+    stage boundaries with; returns the stage names."""
     sm = cfg.sm_scale
-    stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
-              "permute_do", "bsa_bwd", "unpermute_grads"]
-    if not args.block_io:
+    pb32 = P.Problem(pb.T, pb.H, pb.W, pb.heads, pb.head_dim, pb.groups, P.F32)
+    if block_io:
+        stages = ["zone_stats", "assign_shapes", "permute_qkv", "pool", "select", "bsa_fwd", "unpermute_o",
+                  "permute_do", "bsa_bwd", "unpermute_grads"]
+    else:
         stages = ["zone_stats", "assign_shapes", "permute_pool", "select", "bsa_fwd", "bsa_bwd"]
-
-    fixed = P.fixed_shape_index((4, 4, 4)) if args.fixed_shape else None
-    # dense baseline: every key block selected (k = N_b), the same kernels otherwise
-    k_abs, k_frac = (pb.nbmax, 0.0) if args.dense else (cfg.k_abs, cfg.k_frac)
 
     def step(ev=None):
         def mark(i):
@@ -319,7 +336,7 @@ def main():
             mark(1)
             P.prism_fixed_shapes(pb, fixed, L.shape_idx, L.zone_block_off, L.block_start)
         mark(2)
-        if not args.block_io:
+        if not block_io:
             # permute Q, K, V and pool Q, K in one pass; attention outputs straight to token order
             P.prism_permute_pool(pb, L.shape_idx, L.zone_block_off, [q, k, v], [L.qp, L.kp, L.vp],
                                  [L.qbar, L.kbar, None])
@@ -354,33 +371,63 @@ def main():
         P.prism_permute(pb32, L.shape_idx, 1, [L.dqp, L.dkp, L.dvp], [L.dq, L.dk, L.dv])
         mark(10)
 
-    if args.copy_probe_mb > 0:
-        src = torch.ones(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+    return step, stages
+
+
+def measure(cfg, steps, warmup, block_io=False, dense=False, fixed_shape=False, detail=True, inp=None,
+            copy_probe_mb=0):
+    """Time `steps` whole layers (after `warmup`) of one configuration.  Returns a dict of the
+    measurements and, for the caller's CPU baseline, the inputs."""
+    import torch
+
+    import dynamic_block_sparse_var_amd as P
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if inp is None:
+        log(f"bench: config {cfg.name} grid {cfg.T}x{cfg.H}x{cfg.W} heads {cfg.heads} d {cfg.d}; generating inputs")
+        inp = synth.make_inputs(cfg, with_dout=True)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(inp["q"]).to(dt).to(dev)
+    k = torch.from_numpy(inp["k"]).to(dt).to(dev)
+    v = torch.from_numpy(inp["v"]).to(dt).to(dev)
+    do = torch.from_numpy(inp["dout"]).to(dt).to(dev)
+    a = torch.from_numpy(inp["a"]).to(dev)
+    pb = P.make_problem(cfg.T, cfg.H, cfg.W, cfg.heads, cfg.d, cfg.groups, cfg.dtype)
+    L = P.PrismLayer(pb, device=dev, backward=True, token_io=not block_io)
+    fixed = P.fixed_shape_index((4, 4, 4)) if fixed_shape else None
+    # dense baseline: every key block selected (k = N_b), the same kernels otherwise
+    k_abs, k_frac = (pb.nbmax, 0.0) if dense else (cfg.k_abs, cfg.k_frac)
+    step, stages = make_step(P, pb, L, cfg, q, k, v, a, do, block_io, fixed, k_abs, k_frac)
+
+    if copy_probe_mb > 0:
+        src = torch.ones(copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log("bench: warmup")
-    for _ in range(args.warmup):
+    log(f"bench: {cfg.name}: warmup")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # per-kernel events recorded by the library around its own launches
     kev = {kn: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)] for kn in MFMA_KERNELS + HBM_KERNELS}
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+                for _ in range(steps)] for kn in MFMA_KERNELS + HBM_KERNELS}
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for st in range(args.steps):  # make every event a live HIP event before timing
+    for st in range(steps):  # make every event a live HIP event before timing
         for kn in kev:
             for e in kev[kn][st]:
                 e.record()
         for e in sev[st]:
             e.record()
     torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps")
+    log(f"bench: {cfg.name}: timing {steps} steps")
     t_wall = time.perf_counter()
     t_start.record()
-    for st in range(args.steps):
+    for st in range(steps):
         for kn in kev:
             P.prism_trace_kernel(kn, *kev[kn][st])
         step(sev[st])
@@ -388,49 +435,122 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     P.prism_trace_kernel(None)
-    ms_step = t_start.elapsed_time(t_stop) / args.steps
+    ms_step = t_start.elapsed_time(t_stop) / steps
 
-    stage_ms = {s: sum(sev[st][i].elapsed_time(sev[st][i + 1]) for st in range(args.steps)) / args.steps
-                for i, s in enumerate(stages)}
-    kern_ms = {kn: sum(a_.elapsed_time(b_) for a_, b_ in kev[kn]) / args.steps for kn in kev}
+    stage_ms = {s_: sum(sev[st][i].elapsed_time(sev[st][i + 1]) for st in range(steps)) / steps
+                for i, s_ in enumerate(stages)}
+    kern_ms = {kn: sum(a_.elapsed_time(b_) for a_, b_ in kev[kn]) / steps for kn in kev}
 
     pairs, key_frac, hist, nblocks = selection_stats(L, pb)
     d = cfg.d
-    f_fwd = 4.0 * d * pairs
-    f_bwd = 2.5 * f_fwd
     attn_ms = stage_ms["bsa_fwd"] + stage_ms["bsa_bwd"]
-    attn_tflops = (f_fwd + f_bwd) / (attn_ms * 1e-3) / 1e12
-    # matrix-core work actually issued per query-key pair (bf16 path): forward S and the two
-    # halves of the split PV product (3 products of 2d FLOP), dQ kernel S, dP and split dQ (4),
-    # dK/dV kernel S, dP, split dV and split dK (6): 26d against the algorithmic 14d
-    f_exec = 26.0 * d * pairs
-    attn_exec_tflops = f_exec / (attn_ms * 1e-3) / 1e12
-    # algorithmic FLOPs per kernel: forward QK^T + PV; dK/dV kernel S, dP, dV, dK; dQ kernel
-    # only its dQ product (its S and dP are recomputation beyond the five backward GEMMs)
-    kflops = {"k_fwd": 4.0 * d * pairs, "k_dkdv": 8.0 * d * pairs, "k_dq": 2.0 * d * pairs}
+    f_attn = 14.0 * d * pairs          # F_fwd + F_bwd = 4d + 10d per pair
+    res = {"cfg": cfg, "inp": inp, "L": L, "pb": pb, "ms_step": ms_step, "wall": wall, "stage_ms": stage_ms,
+           "kern_ms": kern_ms, "pairs": pairs, "key_frac": key_frac, "hist": hist, "nblocks": nblocks,
+           "attn_ms": attn_ms, "attn_tflops": f_attn / (attn_ms * 1e-3) / 1e12}
+    if detail and cfg.dtype == "bf16":
+        res["fwd_units"], res["atom_units"] = forward_pair_tiles(L, pb)
+    return res
+
+
+def summary(res):
+    """The compact per-configuration record of the `configs` object."""
+    cfg, km = res["cfg"], res["kern_ms"]
+    d, pairs = cfg.d, res["pairs"]
+    out = {"workload": f"{cfg.T}x{cfg.H}x{cfg.W} tokens, {cfg.heads} heads, d {cfg.d}, {cfg.dtype}",
+           "ms_per_layer": round(res["ms_step"], 3),
+           "attn_fwd_bwd_ms": round(res["attn_ms"], 3),
+           "attn_tflops": round(res["attn_tflops"], 1),
+           "attn_mfma_frac": round(res["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+           "stage_ms": {s_: round(x, 4) for s_, x in res["stage_ms"].items()},
+           "selection": {"executed_pairs": pairs, "mean_key_fraction": round(res["key_frac"], 4),
+                         "n_blocks": res["nblocks"]}}
+    if cfg.dtype == "bf16":
+        out["kernel_ms"] = {kn: round(km[kn], 3) for kn in MFMA_KERNELS}
+        dom = max(MFMA_KERNELS, key=lambda kn: km[kn])
+        tf = ALG_PER_PAIR[dom] * d * pairs / (km[dom] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the named configuration (no `configs` object of the other workloads)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a known-size reference "
+                         "for hardware byte counters)")
+    ap.add_argument("--block-io", action="store_true",
+                    help="block-order attention calls with separate permutes of O, dO and the gradients")
+    ap.add_argument("--dense", action="store_true",
+                    help="dense baseline: every key block selected (k = N_b) on the same kernels")
+    ap.add_argument("--fixed-shape", action="store_true",
+                    help="fixed-block ablation: 4x4x4 blocks in every zone, zone statistics and shape "
+                         "assignment skipped")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="no GPU work: read rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs under DIR/FETCH_SIZE and "
+                         "DIR/WRITE_SIZE (taken with --copy-probe-mb on this source tree) and write "
+                         "profiles/traffic.json")
+    args = ap.parse_args()
+    if args.dense and args.fixed_shape:
+        ap.error("--dense and --fixed-shape are separate variants")
+    if args.traffic_from:
+        write_traffic(args.traffic_from, args.copy_probe_mb or 4096, args.config)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is built and measured on one "
+              f"GPU; sharding it by head group over several GPUs is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_block_sparse_var_amd as P
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    res = measure(cfg, args.steps, args.warmup, block_io=args.block_io, dense=args.dense,
+                  fixed_shape=args.fixed_shape, copy_probe_mb=args.copy_probe_mb)
+    L, pb, inp = res["L"], res["pb"], res["inp"]
+    stage_ms, kern_ms, pairs = res["stage_ms"], res["kern_ms"], res["pairs"]
+    dev = torch.device("cuda:0")
+    d = cfg.d
+    attn_ms = res["attn_ms"]
+    attn_tflops = res["attn_tflops"]
+    attn_issued_tflops = sum(ISSUED_PER_PAIR.values()) * d * pairs / (attn_ms * 1e-3) / 1e12
     N, H_ = cfg.N, cfg.heads
     ebytes = 2 if cfg.dtype == "bf16" else 4
     kbytes = {
         "k_zone_stats": N * H_ * d * ebytes + 4 * N,
         "k_pool": 2 * N * H_ * d * ebytes + 2 * H_ * pb.nbmax * d * 4,
     }
-    # Memory side of the attention kernels: the selected-tile stream this dataflow gathers.  For
-    # every (64-row atom, 64-row tile of a block the atom attends to) unit it reads the two bf16
-    # tiles of the other side (K and V; for dK/dV: Q and dO plus their lse2/delta rows), and
-    # each atom's own rows are read or written once.  The forward runs per pair of atoms and
-    # loads each tile of the union of the pair's lists once: (pair, union tile) units.  A
-    # kernel's roofline bound is the side its arithmetic intensity (algorithmic FLOPs per
-    # tile-stream byte) falls on, against the ridge point peak FLOP/s / peak byte/s.
+    # Memory side of the attention kernels (a property of this dataflow, not of the method):
+    # the selected-tile stream.  For every (64-row atom, 64-row tile of a block the atom attends
+    # to) unit a kernel reads the two bf16 tiles of the other side (K and V; for dK/dV: Q and dO
+    # plus their lse2/delta rows); the forward runs per pair of atoms and loads each tile of the
+    # union of the pair's lists once.  unique_io is what each kernel must read and write at
+    # least once: its input tensors and its outputs.
     units = pairs // 4096
-    fwd_units, atom_units = forward_pair_tiles(L, pb)
     atoms = H_ * (N // 64)
     tile = 2 * 64 * d * ebytes
+    fwd_units, atom_units = res.get("fwd_units", units), res.get("atom_units", units)
     kalg = {
         "k_fwd": fwd_units * tile + atoms * (3 * 64 * d * ebytes + 64 * 4),
         "k_dq": units * tile + atoms * (2 * 64 * d * ebytes + 64 * d * 4 + 2 * 64 * 4),
         "k_dkdv": units * (tile + 2 * 64 * 4) + atoms * (2 * 64 * d * ebytes + 2 * 64 * d * 4),
     }
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    row = N * H_ * d
+    unique_io = {
+        "k_fwd": 3 * row * ebytes + 2 * row * ebytes + 4 * N * H_,           # Q, K, V; O and its residual; LSE
+        "k_dq": 4 * row * ebytes + 2 * 4 * N * H_ + 4 * row,                 # Q, K, V, dO; lse2, delta; dQ fp32
+        "k_dkdv": 4 * row * ebytes + 2 * 4 * N * H_ + 2 * 4 * row,           # ...; dK, dV fp32
+    }
     traffic = {}
     tr_path = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tr_path):
@@ -444,26 +564,28 @@ def main():
     attn_k = {}
     for kn in MFMA_KERNELS:
         sec = kern_ms[kn] * 1e-3
-        ai = kflops[kn] / kalg[kn]
+        fl = ALG_PER_PAIR[kn] * d * pairs
         attn_k[kn] = {"ms": round(kern_ms[kn], 3),
-                      "TFLOP/s": round(kflops[kn] / sec / 1e12, 1),
-                      "mfma_frac": round(kflops[kn] / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "TFLOP/s": round(fl / sec / 1e12, 1),
+                      "mfma_frac": round(fl / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "issued_TFLOP/s": round(ISSUED_PER_PAIR[kn] * d * pairs / sec / 1e12, 1),
+                      "unique_io_GB": round(unique_io[kn] / 1e9, 3),
                       "tile_stream_GB": round(kalg[kn] / 1e9, 2),
-                      "GB/s": round(kalg[kn] / sec / 1e9, 1),
-                      "hbm_frac": round(kalg[kn] / sec / 1e9 / PEAK_HBM_GBS, 4),
-                      "flop_per_byte": round(ai, 1),
-                      "bound": "hbm" if ai < ridge else "mfma",
-                      "measured_traffic_GB": round(traffic[kn] / 1e9, 2) if kn in traffic else None}
+                      "tile_stream_GB/s": round(kalg[kn] / sec / 1e9, 1),
+                      "tile_stream_over_unique_io": round(kalg[kn] / unique_io[kn], 1),
+                      "measured_traffic_GB": round(traffic[kn] / 1e9, 2) if kn in traffic else None,
+                      "measured_traffic_over_unique_io": (round(traffic[kn] / unique_io[kn], 1)
+                                                          if kn in traffic else None)}
     # the forward's stream if every atom loaded its own tiles (the dQ walk), for comparison
     attn_k["k_fwd"]["per_atom_stream_GB"] = round((atom_units * tile + (kalg["k_fwd"] - fwd_units * tile)) / 1e9, 2)
+    # Roofline: the attention kernels are matrix-core work; achieved = the dominant kernel's
+    # algorithmic FLOPs per launch (its share of F_fwd + F_bwd) over its mean launch time
     dom = max(MFMA_KERNELS, key=lambda kn: kern_ms[kn])
-    ak = attn_k[dom]
-    if ak["bound"] == "hbm":
-        roof = {"kernel": dom, "bound": "hbm", "achieved": ak["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ak["hbm_frac"], "traffic": traffic.get(dom)}
-    else:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": ak["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ak["mfma_frac"], "traffic": traffic.get(dom)}
+    roof = {"kernel": dom, "bound": "mfma", "achieved": attn_k[dom]["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": attn_k[dom]["mfma_frac"], "traffic": traffic.get(dom),
+            "flop_per_launch": ALG_PER_PAIR[dom] * d * pairs,
+            "attention": {"ms": round(attn_ms, 3), "flop": 14.0 * d * pairs, "TFLOP/s": round(attn_tflops, 1),
+                          "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}}
     if args.block_io:
         # permute of Q, K, V is one launch of k_permute: time it with the stage events around it
         kbytes["k_permute"] = 3 * 2 * N * H_ * d * ebytes
@@ -476,15 +598,20 @@ def main():
     hbm = {kn: {"ms": round(kern_ms[kn], 4), "GB/s": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9, 1),
                 "frac": round(kbytes[kn] / (kern_ms[kn] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
            for kn in hbm_names}
+    # the whole statistics stage (every launch of prism_zone_stats) against its bytes
+    hbm["zone_stats_stage"] = {"ms": round(stage_ms["zone_stats"], 4),
+                               "GB/s": round(kbytes["k_zone_stats"] / (stage_ms["zone_stats"] * 1e-3) / 1e9, 1),
+                               "frac": round(kbytes["k_zone_stats"] / (stage_ms["zone_stats"] * 1e-3) / 1e9
+                                             / PEAK_HBM_GBS, 4)}
 
     out = {
         "metric": "2K-shaped sparse-attn fwd+bwd ms/layer, TFLOP/s and % bf16 MFMA peak",
-        "value": round(ms_step, 3),
+        "value": round(res["ms_step"], 3),
         "unit": "ms/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3),
+        "ms_per_step": round(res["ms_step"], 3),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -500,23 +627,25 @@ def main():
         "attn_fwd_bwd_ms": round(attn_ms, 3),
         "attn_tflops": round(attn_tflops, 1),
         "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "attn_executed_mfma": ({"TFLOP/s": round(attn_exec_tflops, 1),
-                                "frac": round(attn_exec_tflops / PEAK_BF16_TFLOPS, 4),
-                                "note": "matrix-core FLOPs issued: split-bf16 P and dS products and the dQ "
-                                        "kernel's recomputed S and dP included (26d per pair against 14d)"}
-                               if cfg.dtype == "bf16" else None),
-        "stage_ms": {s: round(x, 4) for s, x in stage_ms.items()},
+        "attn_issued_mfma": ({"TFLOP/s": round(attn_issued_tflops, 1),
+                              "frac": round(attn_issued_tflops / PEAK_BF16_TFLOPS, 4),
+                              "issued_over_algorithmic": round(sum(ISSUED_PER_PAIR.values()) / 14.0, 3),
+                              "note": "matrix-core FLOPs issued (split P / dS products and the dQ kernel's "
+                                      "recomputed S and dP included); not the algorithmic rate"}
+                             if cfg.dtype == "bf16" else None),
+        "stage_ms": {s_: round(x, 4) for s_, x in stage_ms.items()},
         "kernel_ms": {kn: round(kern_ms[kn], 4) for kn in MFMA_KERNELS},
         "attn_kernels": attn_k,
         "hbm_stages": hbm,
-        "selection": {"executed_pairs": pairs, "mean_key_fraction": round(key_frac, 4), "n_blocks": nblocks,
-                      "zones_by_volume": {str(kk): vv for kk, vv in hist.items()}},
-        "wall_s_timed": round(wall, 3),
+        "selection": {"executed_pairs": pairs, "mean_key_fraction": round(res["key_frac"], 4),
+                      "n_blocks": res["nblocks"], "zones_by_volume": {str(kk): vv for kk, vv in res["hist"].items()}},
+        "wall_s_timed": round(res["wall"], 3),
         "roofline": roof,
         "cpu_baseline": None,
     }
     # auxiliary, not part of the step: the audio-norm producer (the next layer's coupling input)
     # on a cross-attention output of this GPU's heads x d channels, device-generated
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     hh = torch.randn(N, H_ * d, dtype=dt, device=dev, generator=gen)
@@ -534,7 +663,28 @@ def main():
     out["aux_stages"] = {"audio_norms": {"ms": round(an_ms, 4), "channels": H_ * d,
                                          "GB/s": round(an_bytes / (an_ms * 1e-3) / 1e9, 1),
                                          "frac": round(an_bytes / (an_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
-    del hh, an
+    del hh, an, L
+    res.pop("L")
+    torch.cuda.empty_cache()
+    # the other workloads, each timed the same way with fewer steps (one line, one run)
+    if not args.no_configs and args.config == "2k" and not (args.dense or args.fixed_shape or args.block_io):
+        cfgs = {}
+        for name, steps, warm, kw, reuse in (("720p", 3, 1, {}, False), ("1080p", 3, 1, {}, False),
+                                             ("2k_stress", 2, 1, {}, False),
+                                             ("2k_dense", 1, 1, {"dense": True}, True),
+                                             ("2k_fixed_shape", 3, 1, {"fixed_shape": True}, True),
+                                             ("tiny", 3, 1, {}, False)):
+            c2 = cfg if reuse else synth.CONFIGS[name]
+            r2 = measure(c2, steps, warm, detail=False, inp=inp if reuse else None, **kw)
+            r2.pop("L")
+            sm2 = summary(r2)
+            sm2["steps"] = steps
+            if name == "tiny":
+                sm2["note"] = "fp32 correctness path (one thread per row), not tuned"
+            cfgs[name] = sm2
+            del r2
+            torch.cuda.empty_cache()
+        out["configs"] = cfgs
     if not args.no_cpu_baseline and not (args.dense or args.fixed_shape):
         log("bench: CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(inp, budget_s=args.cpu_seconds)

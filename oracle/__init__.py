@@ -224,6 +224,13 @@ def attn_bwd(q, k, v, dout, block_start, nblocks, groups, sel_count, sel_idx, sm
     return out
 
 
+def last_bwd_phase_seconds():
+    """Wall seconds of the last attn_bwd call's passes: (row statistics, dQ, dK/dV)."""
+    out = np.zeros(3)
+    _load().orc_last_bwd_phase_seconds(_p(out))
+    return tuple(out)
+
+
 def forward_path(inp, groups=1, row_mask=None, nthreads=None):
     """Whole oracle pipeline for one layer on a dict from ``synth.make_inputs``:
     stats -> shapes -> block order -> pooled Q/K -> selection.  Attention is left to the

@@ -8,12 +8,14 @@
  * parallelism is an outer split over independent zones / rows (pthreads), which changes no
  * arithmetic.
  */
+#define _POSIX_C_SOURCE 200809L
 #include "prism_oracle.h"
 
 #include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #define ZONE 8       /* Z_T = Z_H = Z_W = 8 (RG KI, macro-zone partitioning) */
 #define ZVOL 512     /* tokens per zone */
@@ -615,6 +617,19 @@ static void bwd_dkdv_task(void* vctx, int64_t task) {
   }
 }
 
+/* wall seconds of the last orc_attn_bwd's three passes (measurement only) */
+static double g_bwd_phase_s[3];
+
+static double now_s(void) {
+  struct timespec ts;
+  clock_gettime(CLOCK_MONOTONIC, &ts);
+  return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
+void orc_last_bwd_phase_seconds(double* out) {
+  for (int i = 0; i < 3; ++i) out[i] = g_bwd_phase_s[i];
+}
+
 int orc_attn_bwd(int heads, int groups, int N, int d, int nbmax, const int32_t* block_start,
                  const int32_t* nblocks, const int32_t* sel_count, const int32_t* sel_idx,
                  double sm_scale, const float* q, const float* k, const float* v,
@@ -670,16 +685,23 @@ int orc_attn_bwd(int heads, int groups, int N, int d, int nbmax, const int32_t* 
   c.lse = lse; c.delta = delta; c.dq = dq; c.dk = dk; c.dv = dv;
   c.tr_off = tr_off; c.tr_list = tr_list;
   c.row_need = need;
+  double t0 = now_s();
   parallel_for(nthreads, rows, bwd_rowstat_task, &c);
+  double t1 = now_s();
   /* dQ for the requested query blocks */
   c.row_need = dqneed;
   parallel_for(nthreads, rows, bwd_dq_task, &c);
+  double t2 = now_s();
   /* dK, dV for the requested key blocks */
   uint8_t* kmask = (uint8_t*)malloc((size_t)rows);
   if (!kmask) { free(tr_off); free(need); free(dqneed); free(tr_list); free(fill); return -3; }
   for (int64_t kb = 0; kb < rows; ++kb) kmask[kb] = (!kblock_mask || kblock_mask[kb]) ? 1 : 0;
   c.row_need = kmask;
   parallel_for(nthreads, rows, bwd_dkdv_task, &c);
+  double t3 = now_s();
+  g_bwd_phase_s[0] = t1 - t0;
+  g_bwd_phase_s[1] = t2 - t1;
+  g_bwd_phase_s[2] = t3 - t2;
   free(kmask);
   free(tr_off); free(need); free(dqneed); free(tr_list); free(fill);
   return 0;

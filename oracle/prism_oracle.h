@@ -111,6 +111,10 @@ int orc_attn_bwd(int heads, int groups, int N, int d, int nbmax,
                  double* dq, double* dk, double* dv, double* lse, double* delta,
                  int nthreads);
 
+/* Wall-clock seconds of the last orc_attn_bwd call's three passes (row statistics, dQ,
+ * dK/dV), written to out[3]: a measurement aid for the CPU baseline, not part of any result. */
+void orc_last_bwd_phase_seconds(double* out);
+
 /* RG M1 (the audio coupling field is the L2 norm of each video token's audio-to-video
  * cross-attention output, taken from the previous layer).  hhat [N, channels] fp32 (token
  * order) -> a [N] = sqrt(sum_c hhat[n][c]^2), or the sum of squares itself when squared != 0. */
