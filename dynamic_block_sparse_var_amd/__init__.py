@@ -92,6 +92,7 @@ def lib():
                                  _vp]),
         "prism_bsa_bwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
         "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
+        "prism_set_launch_order": (_i32, [_i32]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
         "prism_audio_norms": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp]),
@@ -250,6 +251,11 @@ def prism_bsa_bwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, 
     _check(lib().prism_bsa_bwd_tok(ctypes.byref(pb), _p(shape_idx), _p(block_start), _p(sel_count), _p(sel_idx),
                                    sm_scale, _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk),
                                    _p(dv), _p(workspace), nbytes, _stream(stream)), "prism_bsa_bwd_tok")
+
+
+def prism_set_launch_order(heavy_first: bool):
+    """Heavy units first (True, the default) or the plain launch order (False); process-wide."""
+    _check(lib().prism_set_launch_order(1 if heavy_first else 0), "prism_set_launch_order")
 
 
 def prism_trace_kernel(kernel, start_event=None, stop_event=None):

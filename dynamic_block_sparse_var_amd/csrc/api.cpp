@@ -143,6 +143,13 @@ prism_status prism_trace_kernel(const char* kernel, void* start_event, void* sto
   return PRISM_OK;
 }
 
+prism_status prism_set_launch_order(int32_t heavy_first) {
+  g_err[0] = 0;
+  if (heavy_first != 0 && heavy_first != 1) return fail(PRISM_E_RANGE, "heavy_first = %d must be 0 or 1", heavy_first);
+  set_heavy_first_order(heavy_first == 1);
+  return PRISM_OK;
+}
+
 int32_t prism_shape_table(int32_t* edges) {
   if (!edges) return 0;
   for (int i = 0; i < 16; ++i) {

@@ -399,12 +399,18 @@ static size_t fwd_items_bytes(const Geom& g) {
 }
 size_t bsa_fwd_workspace_bytes(const Geom& g) { return g.bf16 ? 2 * fwd_items_bytes(g) : 0; }
 
+namespace {
+bool g_heavy_first = true;
+}
+bool heavy_first_order() { return g_heavy_first; }
+void set_heavy_first_order(bool on) { g_heavy_first = on; }
+
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* bs, const int32_t* cnt, const int32_t* idx, float sm_scale,
                             const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
                             void* ws, const RowMap& out, hipStream_t st) {
   if (g.bf16) {
     int32_t* order = nullptr;
-    if (ws) {
+    if (ws && heavy_first_order()) {
       // launch order: pairs of atoms with the longest lists first
       order = static_cast<int32_t*>(ws);
       int32_t* work = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + fwd_items_bytes(g));
@@ -446,7 +452,10 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
     if (s != PRISM_OK) return s;
     // dQ: 1.5x the mean; dK/dV: 2.5x, which moves fewer key atoms away from the neighbours that
     // share their query tiles in the L2 (measured: dK/dV -0.8 ms against 1.5x, dQ +0.2 ms at 2.5x)
-    hipLaunchKernelGGL(k_launch_order, dim3(2), dim3(1024), 0, st, order, work, g.heads, (int)(g.N / 64), 15, 25);
+    // with the heavy-first order switched off no unit counts as heavy: the plain order
+    const int off = 1 << 30;
+    hipLaunchKernelGGL(k_launch_order, dim3(2), dim3(1024), 0, st, order, work, g.heads, (int)(g.N / 64),
+                       heavy_first_order() ? 15 : off, heavy_first_order() ? 25 : off);
     s = check_launch("k_launch_order");
     if (s != PRISM_OK) return s;
   }

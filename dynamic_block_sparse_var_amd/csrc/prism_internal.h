@@ -152,6 +152,7 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
 // o_lo.  dout and everything else stay in block order.
 // ws: NULL or bsa_fwd_workspace_bytes(g) bytes of scratch (the launch order of the forward).
 size_t bsa_fwd_workspace_bytes(const Geom& g);
+void set_heavy_first_order(bool on);
 prism_status launch_bsa_fwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
                             const void* v, void* o, void* o_lo, float* lse, void* ws, const RowMap& out,

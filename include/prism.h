@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 2
+#define PRISM_ABI_VERSION 3
 
 typedef enum {
   PRISM_OK = 0,
@@ -189,8 +189,8 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
  * workspace: NULL, or device scratch of at least prism_bsa_fwd_workspace_bytes(pb) bytes,
  *       256-byte aligned, contents on entry irrelevant (workspace_bytes is ignored when NULL).
  *       With it, the workgroups whose query blocks have the longest lists are launched
- *       first (the order is built on the device), which shortens the end of the launch;
- *       the results are the same with or without it. */
+ *       first (the order is built on the device; see prism_set_launch_order), which shortens
+ *       the end of the launch; the results are the same with or without it. */
 size_t prism_bsa_fwd_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
@@ -242,6 +242,13 @@ prism_status prism_bsa_bwd_tok(const prism_problem* pb, const uint8_t* shape_idx
                                const void* o_lo, const void* dout, const float* lse, float* dq,
                                float* dk, float* dv, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* ---- launch order switch ------------------------------------------------------------- *
+ * heavy_first = 1 (the default): the matrix-core attention kernels launch their heaviest units
+ * (pairs of atoms, atoms) first; 0: every launch uses the plain order (atoms of a head in the
+ * XCD-contiguous order).  Results are bitwise the same either way; the switch is process-wide
+ * and not thread-safe, meant for tests and measurements.  PRISM_E_RANGE for other values. */
+prism_status prism_set_launch_order(int32_t heavy_first);
 
 /* ---- measurement hook --------------------------------------------------------------- *
  * Records the HIP events start_event / stop_event (hipEvent_t passed as void*, created by

@@ -17,10 +17,10 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
-    assert P.prism_abi_version() == 2
+    assert P.prism_abi_version() == 3
 
 
 def test_shape_table_matches_oracle_enumeration():
@@ -83,6 +83,12 @@ def test_forward_workspace(L):
     assert P.prism_bsa_fwd_workspace_bytes(_pb(T=3)) == 0
     # fp32 problems run the plain kernels and need none
     assert P.prism_bsa_fwd_workspace_bytes(_pb(dtype=P.F32)) == 0
+
+
+def test_launch_order_switch(L):
+    assert L.prism_set_launch_order(2) == 3
+    assert L.prism_set_launch_order(0) == 0
+    assert L.prism_set_launch_order(1) == 0
 
 
 def test_scalar_ranges_rejected(L):

@@ -198,29 +198,35 @@ def test_empty_lists(run):
 
 
 def test_forward_launch_order_bitwise(run):
-    """The forward's launch order (built in its optional workspace: pairs with the longest
-    lists first) only changes which workgroup runs when: O and LSE are bitwise those of the
-    plain launch order."""
+    """The launch orders (heaviest units first, built on the device in the workspaces) only
+    change which workgroup runs when: O, LSE and the gradients are bitwise those of the plain
+    launch order (prism_set_launch_order(0)); outputs are pre-filled with NaN so a unit that
+    never ran would show."""
     c = run.cfg
     if c.dtype != "bf16":
         pytest.skip("fp32 problems run the plain kernels, without a launch order")
+    from dynamic_block_sparse_var_amd import prism_permute, prism_set_launch_order
+
     run.inject_oracle_plan()
     L = run.layer
-    from dynamic_block_sparse_var_amd import prism_permute
-
     prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
     run.inject_oracle_mask()
-    assert L.fwd_workspace is not None
-    L.attend(c.sm_scale)
-    torch.cuda.synchronize()
-    o1, l1 = L.o.clone(), L.lse.clone()
-    ws, L.fwd_workspace = L.fwd_workspace, None
+    outs = []
     try:
-        L.attend(c.sm_scale)
-        torch.cuda.synchronize()
+        for heavy in (True, False):
+            prism_set_launch_order(heavy)
+            for t in [L.o, L.lse] + ([L.dq, L.dk, L.dv] if run.backward else []):
+                t.fill_(float("nan"))
+            L.attend(c.sm_scale)
+            if run.backward:
+                L.backward(run.dout, c.sm_scale)
+            torch.cuda.synchronize()
+            outs.append([t.clone() for t in [L.o, L.lse] + ([L.dq, L.dk, L.dv] if run.backward else [])])
     finally:
-        L.fwd_workspace = ws
-    assert torch.equal(o1, L.o) and torch.equal(l1, L.lse)
+        prism_set_launch_order(True)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert not torch.isnan(outs[0][0].float()).any()
 
 
 def test_deterministic(run):
