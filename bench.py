@@ -673,7 +673,7 @@ def main():
                                              ("2k_stress", 2, 1, {}, False),
                                              ("2k_dense", 1, 1, {"dense": True}, True),
                                              ("2k_fixed_shape", 3, 1, {"fixed_shape": True}, True),
-                                             ("tiny", 3, 1, {}, False)):
+                                             ("1m", 1, 1, {}, False), ("tiny", 3, 1, {}, False)):
             c2 = cfg if reuse else synth.CONFIGS[name]
             r2 = measure(c2, steps, warm, detail=False, inp=inp if reuse else None, **kw)
             r2.pop("L")

@@ -172,16 +172,16 @@ __global__ __launch_bounds__(64) void k_ref_dkdv(const T* __restrict__ q, const 
   }
 }
 
-constexpr int kMaskColMax = 8 * kMaxZones;  // NBMAX bound: one 32 KB LDS column of mask words
+constexpr int kMaskColMax = 8 * kMaxZones;  // NBMAX bound: one LDS column of mask words (64 KB)
 
 // One workgroup per (word column w, head): the lists of query blocks 32w..32w+31 are ORed into
-// an LDS column of NBMAX words (bit b of word j: block j is in the list of query block 32w + b,
+// an LDS column of NBMAX words (dynamic LDS, 4 * NBMAX bytes) (bit b of word j: block j is in the list of query block 32w + b,
 // LDS atomics, order-free), which is then written out: word [h][j][w] for every j, once.
 __global__ __launch_bounds__(256) void k_mask_t(uint32_t* __restrict__ mask_t, const int32_t* __restrict__ block_start,
                                                 const int32_t* __restrict__ sel_count,
                                                 const int32_t* __restrict__ sel_idx, int nbmax, int nw, int hpg,
                                                 int64_t N) {
-  __shared__ uint32_t col[kMaskColMax];
+  extern __shared__ uint32_t col[];  // nbmax words
   const int w = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
   for (int j = tid; j < nbmax; j += blockDim.x) col[j] = 0u;
@@ -438,8 +438,8 @@ prism_status launch_bsa_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt
   uint32_t* mask_t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + w.mask_off);
   // transposed selection
   if (g.nbmax > kMaskColMax) return fail(PRISM_E_RANGE, "transposed selection: more than %d blocks", kMaskColMax);
-  hipLaunchKernelGGL(k_mask_t, dim3(w.nw, g.heads), dim3(256), 0, st, mask_t, bs, cnt, idx, g.nbmax, w.nw, g.hpg,
-                     g.N);
+  hipLaunchKernelGGL(k_mask_t, dim3(w.nw, g.heads), dim3(256), (size_t)g.nbmax * sizeof(uint32_t), st, mask_t, bs,
+                     cnt, idx, g.nbmax, w.nw, g.hpg, g.N);
   prism_status s = check_launch("k_mask_t");
   if (s != PRISM_OK) return s;
   // launch orders of the matrix-core kernels

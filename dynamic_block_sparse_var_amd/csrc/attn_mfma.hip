@@ -599,10 +599,18 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
     constexpr bool FROM_LDS = decltype(fromc)::value;
     const uint16_t* sK = smem;
     f32x16 sacc = zero16();
+    // K operands four at a time, so one LDS wait covers four products
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const bf16x8 qv = FROM_LDS ? lds_b128(sQB, rowq ^ (st << 4)) : qop[st];
-      sacc = mfma(lds_b128(sK, rowa ^ (st << 4)), qv, sacc);
+    for (int b = 0; b < DS; b += 4) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) ka[st] = lds_b128(sK, rowa ^ ((b + st) << 4));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 qv = FROM_LDS ? lds_b128(sQB, rowq ^ ((b + st) << 4)) : qop[b + st];
+        sacc = mfma(ka[st], qv, sacc);
+      }
     }
     float mx = sacc[0];
 #pragma unroll
@@ -962,10 +970,21 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
 
     // S = Q K^T and dP = dO V^T for this wave's 32 query rows x 32 keys
     f32x16 sacc = zero16(), dpacc = zero16();
+    // operands two steps at a time, so one LDS wait covers four products (more would spill)
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      sacc = mfma(lds_b128(sQ, rowa ^ (st << 4)), kop[st], sacc);
-      dpacc = mfma(lds_b128(sdO, rowa ^ (st << 4)), vop[st], dpacc);
+    for (int b = 0; b < DS; b += 2) {
+      bf16x8 qa[2], da[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        qa[st] = lds_b128(sQ, rowa ^ ((b + st) << 4));
+        da[st] = lds_b128(sdO, rowa ^ ((b + st) << 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        sacc = mfma(qa[st], kop[b + st], sacc);
+        dpacc = mfma(da[st], vop[b + st], dpacc);
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {

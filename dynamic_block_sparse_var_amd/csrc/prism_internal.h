@@ -10,7 +10,7 @@ namespace prism {
 
 constexpr int kZone = 8;      // macro-zone edge (RG KI)
 constexpr int kZoneVol = 512; // tokens per zone
-constexpr int kMaxZones = 1024;  // 8 * Z blocks must fit the selection's LDS sort
+constexpr int kMaxZones = 2048;  // 8 * Z blocks must fit one selection workgroup (64 entries per thread)
 
 // Geometry derived from a validated prism_problem.
 struct Geom {

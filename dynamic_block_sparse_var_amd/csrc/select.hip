@@ -5,7 +5,8 @@
 // rows, sequential fp32 FMA over the head dimension).  The matrix is written into the caller's sel_idx array (same
 // [heads, NBMAX, NBMAX] 4-byte footprint), row by row.
 // k_select: one 256-thread workgroup per (query block, head).  Thread t holds the row's entries
-// j = t + 256q (q < 32) as order-preserving 32-bit score keys and their exp(s - s_max).  The
+// j = t + 256q (q < PER; PER = 32 for rows of up to 8192 blocks, 64 up to 16384) as
+// order-preserving 32-bit score keys and their exp(s - s_max).  The
 // order of the attended-set equation (score descending, block index ascending on ties) is never
 // materialised: the two cuts are found by bisection over the key space, both in the same loop --
 // the k-th largest key (counts from wave ballots) and the largest key whose upper set holds at
@@ -21,7 +22,8 @@ namespace prism {
 
 namespace {
 
-constexpr int kSelMaxKeys = 8192;  // LDS sort capacity (64 KB of 64-bit keys)
+constexpr int kSelThreads = 256;
+constexpr int kSelMaxKeys = 64 * kSelThreads;  // entries a workgroup holds in registers (PER = 64)
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 float* __restrict__ out, const int32_t* __restrict__ block_start,
@@ -95,9 +97,6 @@ __device__ __forceinline__ float unord_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-constexpr int kSelThreads = 256;
-constexpr int kSelPer = kSelMaxKeys / kSelThreads;  // entries per thread
-
 // inclusive scan over the 256 threads of a workgroup (fixed order); part = [4] scratch
 __device__ __forceinline__ int block_incl_scan(int v, int* part) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -113,10 +112,15 @@ __device__ __forceinline__ int block_incl_scan(int v, int* part) {
   return v;
 }
 
+// PER entries per thread: 8 * PER bitmap words per row, PER / 32 of them owned by each thread in
+// the tie ranking and the compaction
+template <int PER>
 __global__ __launch_bounds__(kSelThreads) void k_select(int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
                                                         const int32_t* __restrict__ block_start, int nbmax, int hpg,
                                                         int N, int k_abs, double k_frac, double p) {
-  __shared__ uint32_t sel_bits[kSelMaxKeys / 32], tie_bits[kSelMaxKeys / 32];
+  constexpr int kSelPer = PER;
+  constexpr int WPT = PER / 32;  // bitmap words per thread
+  __shared__ uint32_t sel_bits[8 * PER], tie_bits[8 * PER];
   __shared__ uint32_t red_max[4];
   __shared__ uint32_t red_u[2][4][2];  // per-wave counts, double-buffered across rounds
   __shared__ double red_d[2][4];
@@ -263,23 +267,39 @@ __global__ __launch_bounds__(kSelThreads) void k_select(int32_t* __restrict__ se
     }
   }
   __syncthreads();
-  // thread t owns word t: the tied entries of rank < tneed (in index order) join the selection
-  uint32_t tw = tie_bits[tid], sw = sel_bits[tid];
-  const int tc = __popc(tw);
+  // thread t owns words WPT*t .. WPT*t + WPT - 1: the tied entries of rank < tneed (in index
+  // order) join the selection
+  uint32_t sw[WPT];
+  int tc = 0;
+#pragma unroll
+  for (int x = 0; x < WPT; ++x) {
+    sw[x] = sel_bits[WPT * tid + x];
+    tc += __popc(tie_bits[WPT * tid + x]);
+  }
   int trank = block_incl_scan(tc, part) - tc;
-  while (tw) {
-    const uint32_t b = tw & (0u - tw);
-    tw ^= b;
-    if ((uint32_t)trank < tneed) sw |= b;
-    ++trank;
+#pragma unroll
+  for (int x = 0; x < WPT; ++x) {
+    uint32_t tw = tie_bits[WPT * tid + x];
+    while (tw) {
+      const uint32_t b = tw & (0u - tw);
+      tw ^= b;
+      if ((uint32_t)trank < tneed) sw[x] |= b;
+      ++trank;
+    }
   }
   // ascending compaction
-  const int c = __popc(sw);
+  int c = 0;
+#pragma unroll
+  for (int x = 0; x < WPT; ++x) c += __popc(sw[x]);
   int pos = block_incl_scan(c, part) - c;
-  while (sw) {
-    const int b = __builtin_ctz(sw);
-    sw &= sw - 1u;
-    rowp[pos++] = (tid << 5) + b;
+#pragma unroll
+  for (int x = 0; x < WPT; ++x) {
+    uint32_t w = sw[x];
+    while (w) {
+      const int b = __builtin_ctz(w);
+      w &= w - 1u;
+      rowp[pos++] = ((WPT * tid + x) << 5) + b;
+    }
   }
   if (tid == 0) sel_count[row] = (int32_t)nsel;
 }
@@ -300,8 +320,12 @@ prism_status launch_select(const Geom& g, const int32_t* block_start, const floa
   prism_status s = check_launch("k_scores");
   if (s != PRISM_OK) return s;
   KernelTrace tr("k_select", st);
-  hipLaunchKernelGGL(k_select, dim3(g.nbmax, g.heads), dim3(kSelThreads), 0, st, sel_idx, sel_count, block_start,
-                     g.nbmax, g.hpg, (int)g.N, k_abs, k_frac, p);
+  if (g.nbmax <= 32 * kSelThreads)
+    hipLaunchKernelGGL(k_select<32>, dim3(g.nbmax, g.heads), dim3(kSelThreads), 0, st, sel_idx, sel_count,
+                       block_start, g.nbmax, g.hpg, (int)g.N, k_abs, k_frac, p);
+  else
+    hipLaunchKernelGGL(k_select<64>, dim3(g.nbmax, g.heads), dim3(kSelThreads), 0, st, sel_idx, sel_count,
+                       block_start, g.nbmax, g.hpg, (int)g.N, k_abs, k_frac, p);
   return check_launch("k_select");
 }
 

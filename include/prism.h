@@ -25,8 +25,9 @@
  * - heads are split into `groups` head groups of heads/groups consecutive heads; each group
  *   has its own zone statistics, shapes and block layout; selection and attention are per head.
  * - dtype PRISM_BF16: bf16 tensors, fp32 accumulation.  PRISM_F32: fp32 tensors throughout.
- * - Limits: head_dim in {64, 128}; Z <= 1024 (N <= 524,288 tokens; the selection sorts a
- *   query block's scores in one workgroup's LDS).
+ * - Limits: head_dim in {64, 128}; Z <= 2048 (N <= 1,048,576 tokens: a query block's scores,
+ *   up to NBMAX = 16,384, are held by one selection workgroup, 64 per thread); every tensor
+ *   below 2^31 elements.
  */
 #ifndef PRISM_H
 #define PRISM_H

@@ -45,7 +45,7 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), 2), (dict(T=12), 2), (dict(W=4), 2), (dict(heads=0), 2), (dict(head_dim=96), 2),
-    (dict(groups=3), 2), (dict(dtype=7), 4), (dict(T=8, H=8 * 64, W=8 * 32), 2),
+    (dict(groups=3), 2), (dict(dtype=7), 4), (dict(T=8, H=8 * 64, W=8 * 33), 2),
 ])
 def test_bad_problem_rejected(L, kw, status):
     pb = _pb(**kw)
@@ -164,7 +164,7 @@ def test_token_order_attention_validation(L):
 
 
 def test_selection_capacity_limit(L):
-    # 1024 zones is the largest grid; 1025+ must be refused up front
-    pb = _pb(T=8, H=8 * 32, W=8 * 33)
+    # 2048 zones (1,048,576 tokens) is the largest grid; 2049+ must be refused up front
+    pb = _pb(T=8, H=8 * 32, W=8 * 65)
     assert L.prism_zone_stats(ctypes.byref(pb), FAKE, None, 1e-6, FAKE, FAKE, None, None) == 2
     assert np.isfinite(0.0)

@@ -190,6 +190,34 @@ def test_maximum_block_count_sampled_rows():
     assert hard == 0 and soft <= cap(nrows)
 
 
+def test_largest_block_count_sampled_rows():
+    """16,384 blocks (2048 zones of volume-64 blocks, the selection's capacity: 64 entries per
+    thread), k 5 %, p 0.9, on a sample of rows that the oracle computes."""
+    T, H, W = 16, 128, 512
+    heads, d = 1, 128
+    bs, nb = _layout(T, H, W, 3)
+    nbmax, n = bs.shape[1] - 1, int(nb[0])
+    assert n == 16384
+    rng = np.random.default_rng(4650)
+    qbar, kbar = _pooled(rng, heads, nbmax, n, d, 0.3), _pooled(rng, heads, nbmax, n, d, 0.3)
+    sm = 16.0 / math.sqrt(d)
+    rows = np.zeros((heads, nbmax), np.uint8)
+    rows[0, rng.choice(n, 96, replace=False)] = 1
+    rows[0, [0, 8191, 8192, n - 1]] = 1
+    gc, gi = _gpu_select(T, H, W, heads, d, bs, qbar, kbar, sm, 0, 0.05, 0.9)
+    oc, oi, info = _oracle_select(qbar, kbar, nb, sm, 0, 0.05, 0.9, rows=rows)
+    hard, soft, nrows = compare_masks(gc, gi, oc, oi, info, nb, 1, rows_mask=rows, **_scores(qbar, kbar, sm))
+    report(f"select edges 16384 blocks: {nrows} rows, mean |S| {oc[0][rows[0] == 1].mean():.1f}, hard {hard}, "
+           f"near-tie {soft}")
+    assert hard == 0 and soft <= cap(nrows)
+    # uniform scores over 16,384 blocks: the lowest max(k, ceil(p N_b)) indices, on every row
+    q0 = np.zeros_like(qbar)
+    gc, gi = _gpu_select(T, H, W, heads, d, bs, q0, kbar, sm, 7, 0.0, 0.3711)
+    want = max(7, math.ceil(0.3711 * n))
+    assert (gc[0, :n] == want).all()
+    assert all(np.array_equal(gi[0, i, :want], np.arange(want)) for i in (0, 1, 8191, 8192, n - 1))
+
+
 def test_two_blocks():
     """Smallest layout: one zone of two volume-256 blocks."""
     heads, d = 2, 64
