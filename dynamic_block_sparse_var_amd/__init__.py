@@ -93,6 +93,9 @@ def lib():
         "prism_bsa_bwd_workspace_bytes": (ctypes.c_size_t, [_PB]),
         "prism_trace_kernel": (_i32, [ctypes.c_char_p, _vp, _vp]),
         "prism_set_launch_order": (_i32, [_i32]),
+        "prism_bsa_bwd_noalloc_max_bytes": (ctypes.c_size_t, []),
+        "prism_bsa_bwd_noalloc": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp]),
         "prism_bsa_bwd": (_i32, [_PB, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
         "prism_audio_norms": (_i32, [_PB, _vp, _i32, _i32, _vp, _vp]),
@@ -231,6 +234,18 @@ def prism_bsa_bwd(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_l
     _check(lib().prism_bsa_bwd(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale, _p(q), _p(k),
                                _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk), _p(dv), _p(workspace),
                                nbytes, _stream(stream)), "prism_bsa_bwd")
+
+
+def prism_bsa_bwd_noalloc_max_bytes() -> int:
+    return int(lib().prism_bsa_bwd_noalloc_max_bytes())
+
+
+def prism_bsa_bwd_noalloc(pb, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, dout, lse, dq, dk, dv,
+                          stream=None):
+    """prism_bsa_bwd without a workspace argument: the library's fixed per-device scratch."""
+    _check(lib().prism_bsa_bwd_noalloc(ctypes.byref(pb), _p(block_start), _p(sel_count), _p(sel_idx), sm_scale,
+                                       _p(q), _p(k), _p(v), _p(o), _p(o_lo), _p(dout), _p(lse), _p(dq), _p(dk),
+                                       _p(dv), _stream(stream)), "prism_bsa_bwd_noalloc")
 
 
 def prism_bsa_fwd_tok(pb, shape_idx, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, o_lo, lse, workspace=None,

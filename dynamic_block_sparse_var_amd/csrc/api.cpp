@@ -366,6 +366,40 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start, 
                         lse, dq, dk, dv, workspace, block_rows(), block_rows(), (hipStream_t)stream);
 }
 
+prism_status prism_bsa_bwd_noalloc(const prism_problem* pb, const int32_t* block_start, const int32_t* sel_count,
+                                   const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
+                                   const void* v, const void* o, const void* o_lo, const void* dout,
+                                   const float* lse, float* dq, float* dk, float* dv, void* stream) {
+  g_err[0] = 0;
+  PRISM_TRY(validate_problem(pb));
+  PRISM_TRY(need_aligned(block_start, "block_start"));
+  PRISM_TRY(need_aligned(sel_count, "sel_count"));
+  PRISM_TRY(need_aligned(sel_idx, "sel_idx"));
+  PRISM_TRY(need_aligned(q, "q"));
+  PRISM_TRY(need_aligned(k, "k"));
+  PRISM_TRY(need_aligned(v, "v"));
+  PRISM_TRY(need_aligned(o, "o"));
+  if (o_lo) PRISM_TRY(need_aligned(o_lo, "o_lo"));
+  PRISM_TRY(need_aligned(dout, "dout"));
+  PRISM_TRY(need_aligned(lse, "lse"));
+  PRISM_TRY(need_aligned(dq, "dq"));
+  PRISM_TRY(need_aligned(dk, "dk"));
+  PRISM_TRY(need_aligned(dv, "dv"));
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return fail(PRISM_E_RANGE, "sm_scale = %g must be finite and > 0", (double)sm_scale);
+  Geom gm = make_geom(pb);
+  const size_t need = bsa_bwd_workspace_bytes(gm);
+  if (need > kNoAllocScratchBytes)
+    return fail(PRISM_E_WORKSPACE, "backward needs %zu bytes of scratch, the allocation-free entry point has %zu",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  PRISM_TRY(noalloc_scratch(&ws));
+  return launch_bsa_bwd(gm, block_start, sel_count, sel_idx, sm_scale, q, k, v, o, gm.bf16 ? o_lo : nullptr, dout,
+                        lse, dq, dk, dv, ws, block_rows(), block_rows(), (hipStream_t)stream);
+}
+
+size_t prism_bsa_bwd_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
 // ---- token-order interface of the attention ---------------------------------------------
 
 prism_status prism_bsa_fwd_tok(const prism_problem* pb, const uint8_t* shape_idx, const int32_t* block_start,

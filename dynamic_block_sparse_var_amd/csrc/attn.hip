@@ -13,6 +13,8 @@
 //                the launch orders of the matrix-core dQ and dK/dV kernels (heavy atoms first).
 #include <math.h>
 
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace prism {
@@ -372,6 +374,30 @@ prism_status run_ref_bwd(const Geom& g, const int32_t* bs, const int32_t* cnt, c
 }
 
 }  // namespace
+
+// The allocation-free backward's workspace: a file-scope device array, one copy per device the
+// library runs on, held until the process ends.  Host code never uses its name as an address
+// (on the host it is only a stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+prism_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  prism_status s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (s != PRISM_OK) return s;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PRISM_E_RANGE, "device %d beyond the library's %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    s = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (s != PRISM_OK) return s;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PRISM_OK;
+}
 
 BwdWorkspace bwd_workspace_layout(const Geom& g) {
   BwdWorkspace w;

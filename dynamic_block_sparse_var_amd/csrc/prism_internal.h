@@ -158,6 +158,11 @@ prism_status launch_bsa_fwd(const Geom& g, const int32_t* block_start, const int
                             const void* v, void* o, void* o_lo, float* lse, void* ws, const RowMap& out,
                             hipStream_t st);
 size_t bsa_bwd_workspace_bytes(const Geom& g);
+// The allocation-free backward (prism_bsa_bwd_noalloc): its workspace is a device array of
+// kNoAllocScratchBytes per device; noalloc_scratch gives the current device's copy.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+prism_status noalloc_scratch(void** out);
 prism_status launch_bsa_bwd(const Geom& g, const int32_t* block_start, const int32_t* sel_count,
                             const int32_t* sel_idx, float sm_scale, const void* q, const void* k,
                             const void* v, const void* o, const void* o_lo, const void* dout,

@@ -218,6 +218,23 @@ prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
                            float* dk, float* dv, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* ---- a7 without allocation ---------------------------------------------------------- *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): prism_bsa_bwd with the same arguments and results,
+ * minus the workspace, which is a fixed device array inside the library instead, of
+ * prism_bsa_bwd_noalloc_max_bytes() bytes (64 MiB; each device the library runs on holds one
+ * copy until the process ends).  Problems whose prism_bsa_bwd_workspace_bytes exceed it are
+ * refused with PRISM_E_WORKSPACE before anything is launched (the 2K-shaped problem, 4 heads,
+ * needs about 46 MB).  The call allocates nothing.  Every call on one device shares that
+ * device's array, whose contents on entry do not matter: calls that overlap on one device
+ * (different streams, threads) race on it and must be serialised by the caller. */
+size_t prism_bsa_bwd_noalloc_max_bytes(void);
+prism_status prism_bsa_bwd_noalloc(const prism_problem* pb, const int32_t* block_start,
+                                   const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
+                                   const void* q, const void* k, const void* v, const void* o,
+                                   const void* o_lo, const void* dout, const float* lse, float* dq,
+                                   float* dk, float* dv, void* stream);
+
 /* ---- a6 / a7 with token-order outputs ------------------------------------------------ *
  * The same attention as prism_bsa_fwd / prism_bsa_bwd, with the caller-facing tensors in token
  * order [N, heads, head_dim]: the kernels write each output row straight to its token (the

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = P.header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert P.prism_abi_version() == 3
@@ -83,6 +83,21 @@ def test_forward_workspace(L):
     assert P.prism_bsa_fwd_workspace_bytes(_pb(T=3)) == 0
     # fp32 problems run the plain kernels and need none
     assert P.prism_bsa_fwd_workspace_bytes(_pb(dtype=P.F32)) == 0
+
+
+def test_noalloc_backward_refuses_beyond_its_scratch(L):
+    """prism_bsa_bwd_noalloc: the 2K-shaped problem fits its fixed 64 MiB scratch, the largest
+    grid does not and is refused with PRISM_E_WORKSPACE before any launch."""
+    assert P.prism_bsa_bwd_noalloc_max_bytes() == 64 << 20
+    assert P.prism_bsa_bwd_workspace_bytes(_pb(T=32, H=96, W=160, heads=4, head_dim=128)) <= 64 << 20
+    big = _pb(T=64, H=128, W=128, heads=4, head_dim=128)
+    assert P.prism_bsa_bwd_workspace_bytes(big) > 64 << 20
+    args = [ctypes.byref(big)] + [FAKE] * 3 + [0.125] + [FAKE] * 10 + [None]
+    assert L.prism_bsa_bwd_noalloc(*args) == 6
+    assert "scratch" in L.prism_last_error().decode()
+    small = _pb()
+    args = [ctypes.byref(small)] + [FAKE] * 3 + [0.125] + [FAKE] * 4 + [MISALIGNED] + [FAKE] * 5 + [None]
+    assert L.prism_bsa_bwd_noalloc(*args) == 5
 
 
 def test_launch_order_switch(L):
