@@ -29,8 +29,8 @@ COMMON = [
 ]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], bdir: str = BUILD) -> str:
+    obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -42,25 +42,36 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int | None = None, extra: list[str] | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source into `out` (default: the package's libprism.so); objects of a build
+    with extra flags go to a build folder of their own."""
     extra = list(extra or [])
+    out = out or LIB
+    bdir = BUILD if not extra or extra == ["-Rpass-analysis=kernel-resource-usage"] else BUILD + "_" + "_".join(
+        f.strip("-").replace("=", "_") for f in extra)
+    os.makedirs(bdir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, bdir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--resource-usage", action="store_true", help="print per-kernel register/LDS usage")
+    ap.add_argument("--debug", action="store_true",
+                    help="bounds-checked build: the kernels assert that every row, tile and list entry they touch "
+                         "lies inside its tensor (PRISM_DEBUG)")
+    ap.add_argument("--out", default=None, help="library path (default: the package's libprism.so)")
     a = ap.parse_args()
     ex = ["-Rpass-analysis=kernel-resource-usage"] if a.resource_usage else []
-    print(build(a.jobs, ex))
+    if a.debug:
+        ex.append("-DPRISM_DEBUG")
+    print(build(a.jobs, ex, out=a.out))

@@ -15,11 +15,6 @@ struct BwdWorkspace {
   int nw, items;
 };
 
-// Atoms of one head in launch order, spread so that each XCD (workgroup id mod 8) walks a
-// contiguous range: launch position x of a head's natoms workgroups takes atom xcd_atom(x).
-__device__ __forceinline__ int xcd_atom(int x, int natoms) {
-  return ((natoms & 7) == 0) ? (x & 7) * (natoms >> 3) + (x >> 3) : x;
-}
 BwdWorkspace bwd_workspace_layout(const Geom& g);
 
 // order: NULL (plain launch order) or the forward's launch order, items = head * N/128 + pair

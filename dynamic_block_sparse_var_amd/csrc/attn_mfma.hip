@@ -110,40 +110,18 @@ __device__ __forceinline__ u32x2 lds_tr(const uint16_t* p) {
 }
 
 // ---- swizzled, unpadded 64 x D tiles filled by direct global -> LDS loads -----------------
-//
-// Row r occupies 2*D contiguous bytes; its 16-byte chunk c sits in chunk slot c ^ swz(r).  The
-// swizzle makes both read patterns bank-conflict free: 16 consecutive rows at one chunk
-// (ds_read_b128 operands) and 4 consecutive rows x 4 consecutive chunks (ds_read_b64_tr_b16).
+// (layout, swizzle and addresses: index_math.h)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
-
-template <int D>
-struct Tile {
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;      // rows per 1 KB load
-  static constexpr int NI = 16 / RPI;       // 1 KB loads per wave per tile (4 waves)
-  static constexpr int ELEMS = 64 * D;
-};
-
 // Staging a 64-row tile: each of the 4 waves issues NI loads of 1 KB (global_load_lds_dwordx4,
-// one 16-byte chunk per lane).  The hardware puts lane l's chunk at byte 16*l after the wave's
-// LDS base, so the lane fetches the chunk whose swizzled slot that is; off[i] is its byte
-// offset from the start of the source rows.  Completion is awaited with dma_wait() before the
-// workgroup barrier.
+// one 16-byte chunk per lane) from the byte offsets off[i] = dma_src_offset(w, lane, i).
+// Completion is awaited with dma_wait() before the workgroup barrier.
 template <int D>
 __device__ __forceinline__ void dma_offsets(int w, int lane, uint32_t (&off)[Tile<D>::NI]) {
-  using TL = Tile<D>;
 #pragma unroll
-  for (int i = 0; i < TL::NI; ++i) {
-    const int r = (w * TL::NI + i) * TL::RPI + lane / TL::CPR;
-    off[i] = r * 2 * D + (((lane % TL::CPR) ^ swz<D>(r)) << 4);
-  }
+  for (int i = 0; i < Tile<D>::NI; ++i) off[i] = dma_src_offset<D>(w, lane, i);
 }
 
 template <int D>
@@ -158,23 +136,10 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint1
 
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Byte addresses.  A b128 read of chunk c of row r is at row_addr(r) ^ (c << 4).  The two
-// transposing reads of tile_rows_op at rows R0.. (R0 % 16 == 0) and columns D0.. (D0 % 32 == 0)
-// are at (tr[b] ^ (2 * D0)) + 2 * D * R0, tr[] being the lane's addresses for R0 = D0 = 0.
 template <int D>
-__device__ __forceinline__ uint32_t row_addr(int r) {
-  return r * 2 * D + (swz<D>(r) << 4);
-}
-
-template <int D>
-__device__ __forceinline__ void tr_addr(int lane, uint32_t (&tr)[2]) {
-  const int j = lane & 15;
-  const int col = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int row = 4 * (lane >> 5) + (j >> 2) + 8 * b;
-    tr[b] = row * 2 * D + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
-  }
+__device__ __forceinline__ void tr_addrs(int lane, uint32_t (&tr)[2]) {
+  tr[0] = tr_addr<D>(lane, 0);
+  tr[1] = tr_addr<D>(lane, 1);
 }
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* s, uint32_t byte) {
@@ -194,7 +159,7 @@ __device__ __forceinline__ bf16x8 lds_b128(const uint16_t* s, uint32_t byte) {
 template <int D>
 __device__ __forceinline__ void tr_table(const uint16_t* smem, int lane, int Rw, uint32_t (&a)[2]) {
   uint32_t tr[2];
-  tr_addr<D>(lane, tr);
+  tr_addrs<D>(lane, tr);
   const uint32_t sbase = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)smem);
 #pragma unroll
   for (int b = 0; b < 2; ++b) a[b] = sbase + tr[b] + 2 * D * Rw;
@@ -340,6 +305,7 @@ struct MaskTiles {
     const int bit = __builtin_ctz(bits);
     bits &= bits - 1;
     const int qb = ((base + k) << 5) + bit;
+    PRISM_ASSERT(qb < nw * 32);
     rt = bs[qb];
     rend = bs[qb + 1];
   }
@@ -557,6 +523,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   int rowA, rowB;
   pair_atoms(bs, nbmax, sel_count + (int64_t)h * nbmax, sel_idx + (int64_t)h * nbmax * nbmax, pidx,
              reinterpret_cast<uint32_t*>(smem), rowA, rowB);
+  PRISM_ASSERT(rowA >= 0 && rowB >= 0 && rowA + 64 <= N && rowB + 64 <= N && !(rowA & 63) && !(rowB & 63));
   const int qa = block_of_row(bs, nbmax, rowA), qb = block_of_row(bs, nbmax, rowB);
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
@@ -590,6 +557,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(const uint16_t* __restrict__ Q, 
   uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
   const uint32_t rowq = row_addr<D>(32 * rh + l32) ^ ((CH * half) << 4);
   auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
+    PRISM_ASSERT(it.kt >= 0 && it.kt + 64 <= N);
     uint16_t* s = smem + soff / 2;
     dma_tile<D>(Kh + (int64_t)it.kt * D, s, w, doff);
     dma_tile<D>(Vh + (int64_t)it.kt * D, s + T, w, doff);
@@ -760,6 +728,7 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
   const int h = item / natoms;
   const int row0 = (item - h * natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  PRISM_ASSERT(h < gridDim.y && row0 >= 0 && row0 + 64 <= N);
   const int qb = block_of_row(bs, nbmax, row0);
   const int64_t hoff = (int64_t)h * N * D;
   const uint16_t* Kh = K + hoff;
@@ -790,6 +759,7 @@ __global__ __launch_bounds__(256, 2) void k_dq(const uint16_t* __restrict__ Q, c
   // per-lane read addresses of the stage being computed (moved to the other stage per tile)
   uint32_t rowa = row_addr<D>(32 * kh + l32) ^ ((CH * half) << 4);
   auto stage = [&](uint32_t soff) __attribute__((always_inline)) {
+    PRISM_ASSERT(it.kt >= 0 && it.kt + 64 <= N);
     uint16_t* s = smem + soff / 2;
     dma_tile<D>(Kh + (int64_t)it.kt * D, s, w, doff);
     dma_tile<D>(Vh + (int64_t)it.kt * D, s + T, w, doff);
@@ -915,6 +885,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
   const int h = item / natoms;
   const int key0 = (item - h * natoms) * 64;
   const int32_t* bs = block_start + (int64_t)(h / hpg) * (nbmax + 1);
+  PRISM_ASSERT(h < gridDim.y && key0 >= 0 && key0 + 64 <= N);
   const int kb_idx = block_of_row(bs, nbmax, key0);
   const int64_t hoff = (int64_t)h * N * D;
   const int mykey = key0 + 32 * kh + l32;
@@ -957,6 +928,7 @@ __global__ __launch_bounds__(256, 2) void k_dkdv(const uint16_t* __restrict__ Q,
     asm volatile("" : "+v"(ln));
     uint32_t doff[Tile<D>::NI];
     dma_offsets<D>(w, ln, doff);
+    PRISM_ASSERT(it.rt >= 0 && it.rt + 64 <= N);
     uint16_t* s = smem + soff / 2;
     if (w < 2)
       __builtin_amdgcn_global_load_lds((gbl_void*)(ldsrc + it.rt + 4 * (ln & 15)),

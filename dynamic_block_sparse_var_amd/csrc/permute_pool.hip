@@ -20,7 +20,6 @@ struct PermPtrs {
   uint8_t* dst[4];
 };
 
-__device__ __forceinline__ int ilog2_small(int x) { return x == 2 ? 1 : x == 4 ? 2 : 3; }
 
 template <int CPR_LOG2>  // log2 of 16-byte chunks per row
 __global__ __launch_bounds__(256) void k_permute(PermPtrs pp, const uint8_t* __restrict__ shape_idx, int inverse,
@@ -31,7 +30,7 @@ __global__ __launch_bounds__(256) void k_permute(PermPtrs pp, const uint8_t* __r
   const int zt = m / (ZH * ZW), zh = (m / ZW) % ZH, zw = m % ZW;
   const int s = shape_idx[(int64_t)grp * Z + m];
   const int bT = c_shapes[s].bT, bH = c_shapes[s].bH, bW = c_shapes[s].bW;
-  const int lT = ilog2_small(bT), lH = ilog2_small(bH), lW = ilog2_small(bW);
+  const int lT = ilog2_edge(bT), lH = ilog2_edge(bH), lW = ilog2_edge(bW);
   const int lB = lT + lH + lW;
   const int lnW = 3 - lW, lnH = 3 - lH;  // log2 of blocks along W and H inside the zone
   const uint8_t* src = pp.src[tsel];

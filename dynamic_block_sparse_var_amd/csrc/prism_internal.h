@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/prism.h"
+#include "index_math.h"
 
 namespace prism {
 
@@ -80,31 +81,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// Largest j in [0, nbmax) with bs[j] <= row (bs ascending, bs[j] = N past the last block).
-__device__ __forceinline__ int block_of_row(const int32_t* bs, int nbmax, int row) {
-  int lo = 0, hi = nbmax - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (bs[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Token of a block-order row.  Position p (0..511) of zone m's block-order range, the zone's
-// blocks having edges (bT, bH, bW) in {2, 4, 8}: blocks in raster order over the zone's block
-// grid, tokens in raster order inside a block.  Returns n = (t*H + h)*W + w.
-__device__ __forceinline__ int ilog2_edge(int x) { return x == 2 ? 1 : x == 4 ? 2 : 3; }
-__device__ __forceinline__ int64_t zone_pos_token(int m, int p, int bT, int bH, int bW, int H, int W, int ZH,
-                                                  int ZW) {
-  const int lT = ilog2_edge(bT), lH = ilog2_edge(bH), lW = ilog2_edge(bW);
-  const int lB = lT + lH + lW, lnW = 3 - lW, lnH = 3 - lH;
-  const int beta = p >> lB, iota = p & ((1 << lB) - 1);
-  const int bw = beta & ((1 << lnW) - 1), bh = (beta >> lnW) & ((1 << lnH) - 1), bt = beta >> (lnW + lnH);
-  const int iw = iota & (bW - 1), ih = (iota >> lW) & (bH - 1), it = iota >> (lW + lH);
-  const int zt = m / (ZH * ZW), zh = (m / ZW) % ZH, zw = m % ZW;
-  return ((int64_t)(zt * 8 + (bt << lT) + it) * H + zh * 8 + (bh << lH) + ih) * W + zw * 8 + (bw << lW) + iw;
 }
 
 // Where the attention kernels put an output row: block order [heads, N, d] when shape_idx is

@@ -298,6 +298,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(int32_t* __restrict__ se
     while (w) {
       const int b = __builtin_ctz(w);
       w &= w - 1u;
+      PRISM_ASSERT(pos < nb && ((WPT * tid + x) << 5) + b < nb);
       rowp[pos++] = ((WPT * tid + x) << 5) + b;
     }
   }
