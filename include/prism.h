@@ -191,7 +191,9 @@ prism_status prism_select_blocks(const prism_problem* pb, const int32_t* block_s
  *       256-byte aligned, contents on entry irrelevant (workspace_bytes is ignored when NULL).
  *       With it, the workgroups whose query blocks have the longest lists are launched
  *       first (the order is built on the device; see prism_set_launch_order), which shortens
- *       the end of the launch; the results are the same with or without it. */
+ *       the end of the launch; the results are the same with or without it.  After a bf16
+ *       call its first heads*N/128 int32 hold that order (items head*N/128 + pair), followed,
+ *       256-byte aligned, by the per-pair work estimates it was built from. */
 size_t prism_bsa_fwd_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,
@@ -209,7 +211,12 @@ prism_status prism_bsa_fwd(const prism_problem* pb, const int32_t* block_start,
  *       matrix-core products with P and dS split each factor into a bf16 head and a bf16
  *       residual, so the gradients keep fp32-level accuracy.
  * workspace: device scratch of at least prism_bsa_bwd_workspace_bytes(pb) bytes, 256-byte
- * aligned; its contents on entry do not matter. */
+ * aligned; its contents on entry do not matter.  After a bf16 call it holds (each part starting
+ * 256-byte aligned, A(x) = x rounded up to a multiple of 256): delta [heads, N] fp32 at 0;
+ * lse2 = LSE * log2(e) at A(4*heads*N); the transposed selection bitmap [heads, NBMAX,
+ * ceil(NBMAX/32)] uint32 at 2*A(4*heads*N); then the launch orders of the dQ and dK/dV
+ * kernels [2][heads*N/64] int32 and the per-atom work estimates they were built from
+ * [2][heads*N/64] int32 (readable for inspection; see prism_set_launch_order). */
 size_t prism_bsa_bwd_workspace_bytes(const prism_problem* pb);
 prism_status prism_bsa_bwd(const prism_problem* pb, const int32_t* block_start,
                            const int32_t* sel_count, const int32_t* sel_idx, float sm_scale,

@@ -176,6 +176,74 @@ def test_attention_full_sampled(run):
         assert rel < 1e-4 and dk_sum <= 1e-4 * dk_scale
 
 
+def _expected_order(work, heads, units, f):
+    """The documented launch order: units of each head in XCD-contiguous order, those whose work
+    exceeds f/10 times the mean first, both parts keeping that order."""
+    def xcd(x, n):
+        return (x & 7) * (n >> 3) + (x >> 3) if n % 8 == 0 else x
+    plain = [(t // units) * units + xcd(t % units, units) for t in range(heads * units)]
+    n, total = heads * units, int(work.sum())
+    heavy = [it for it in plain if 10 * int(work[it]) * n > f * total]
+    light = [it for it in plain if not 10 * int(work[it]) * n > f * total]
+    return np.array(heavy + light, np.int64), len(heavy)
+
+
+def test_launch_orders_read_back(run):
+    """The launch orders the attention builds in its workspaces, read back at full size (where a
+    thread of the order kernel partitions many units): each is the documented partition of the
+    plain XCD-contiguous order -- units with more than 1.5x (forward pairs, dQ atoms) or 2.5x
+    (dK/dV atoms) the mean work first -- built from work estimates that match the selection."""
+    c, o = run.cfg, run.orc
+    if not run.backward:
+        pytest.skip("forward-only config")
+    run.inject_oracle_plan()
+    L = run.layer
+    from dynamic_block_sparse_var_amd import prism_permute
+
+    prism_permute(run.pb, L.shape_idx, 0, [run.q, run.k, run.v], [L.qp, L.kp, L.vp])
+    run.inject_oracle_mask()
+    L.attend(c.sm_scale)
+    L.backward(run.dout, c.sm_scale)
+    torch.cuda.synchronize()
+    A = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    heads, N = c.heads, c.N
+    nb = int(o["nblocks"][0])
+    bs = o["block_start"][0].astype(np.int64)
+    cnt = o["sel_count"][:, :nb].astype(np.int64)
+    col = np.stack([attn_rows.selector_counts(o["sel_count"], o["sel_idx"], nb, h) for h in range(heads)])
+    # backward: per atom, its block's list length (dQ) and selector count (dK/dV)
+    items = heads * (N // 64)
+    ws = L.workspace.cpu().numpy()
+    nw = (c.nbmax + 31) // 32
+    off = 2 * A(4 * heads * N) + A(4 * heads * c.nbmax * nw)
+    order = ws[off:off + 8 * items].view(np.int32).reshape(2, items)
+    work = ws[off + A(8 * items):off + A(8 * items) + 8 * items].view(np.int32).reshape(2, items)
+    blk = np.searchsorted(bs[:nb + 1], np.arange(0, N, 64), side="right") - 1
+    np.testing.assert_array_equal(work[0].reshape(heads, -1), cnt[:, blk])
+    np.testing.assert_array_equal(work[1].reshape(heads, -1), col[:, blk])
+    for side, f in ((0, 15), (1, 25)):
+        want, nheavy = _expected_order(work[side].astype(np.int64), heads, N // 64, f)
+        np.testing.assert_array_equal(order[side], want)
+        assert np.array_equal(np.sort(order[side]), np.arange(items))
+        say(f"  {c.name}: {'dQ' if side == 0 else 'dK/dV'} launch order: {nheavy} of {items} atoms first")
+    # forward: pairs of atoms, work twice the zone's longest list (zones of 64-row blocks) or twice
+    # the pair's block list
+    pairs = heads * (N // 128)
+    fw = L.fwd_workspace.cpu().numpy()
+    forder = fw[:4 * pairs].view(np.int32)
+    fwork = fw[A(4 * pairs):A(4 * pairs) + 4 * pairs].view(np.int32).reshape(heads, -1)
+    j0 = np.searchsorted(bs[:nb + 1], np.arange(0, N, 512), side="right") - 1
+    small = (bs[j0 + 1] - bs[j0]) == 64
+    for h in range(heads):
+        zw = np.where(small, np.max(np.stack([cnt[h, np.minimum(j0 + q, nb - 1)] for q in range(8)]), 0), 0)
+        for s_ in range(4):
+            big = cnt[h, np.minimum(j0 + (128 * s_) // np.maximum(bs[j0 + 1] - bs[j0], 1), nb - 1)]
+            np.testing.assert_array_equal(fwork[h, s_::4], 2 * np.where(small, zw, big))
+    want, nheavy = _expected_order(fwork.reshape(-1).astype(np.int64), heads, N // 128, 15)
+    np.testing.assert_array_equal(forder, want)
+    say(f"  {c.name}: forward launch order: {nheavy} of {pairs} pairs first")
+
+
 def test_token_order_path_full(run):
     """The path the benchmark times (one-pass permute+pool, token-order attention) at full size:
     bitwise equal to the block-order calls plus permutes, whose parity the tests above check,
