@@ -445,8 +445,8 @@ def measure(cfg, steps, warmup, block_io=False, dense=False, fixed_shape=False, 
     d = cfg.d
     attn_ms = stage_ms["bsa_fwd"] + stage_ms["bsa_bwd"]
     f_attn = 14.0 * d * pairs          # F_fwd + F_bwd = 4d + 10d per pair
-    res = {"cfg": cfg, "inp": inp, "L": L, "pb": pb, "ms_step": ms_step, "wall": wall, "stage_ms": stage_ms,
-           "kern_ms": kern_ms, "pairs": pairs, "key_frac": key_frac, "hist": hist, "nblocks": nblocks,
+    res = {"cfg": cfg, "inp": inp, "L": L, "pb": pb, "dev_tensors": (q, k, v, a), "ms_step": ms_step,
+           "wall": wall, "stage_ms": stage_ms, "kern_ms": kern_ms, "pairs": pairs, "key_frac": key_frac, "hist": hist, "nblocks": nblocks,
            "attn_ms": attn_ms, "attn_tflops": f_attn / (attn_ms * 1e-3) / 1e12}
     if detail and cfg.dtype == "bf16":
         res["fwd_units"], res["atom_units"] = forward_pair_tiles(L, pb)
@@ -518,6 +518,7 @@ def main():
     res = measure(cfg, args.steps, args.warmup, block_io=args.block_io, dense=args.dense,
                   fixed_shape=args.fixed_shape, copy_probe_mb=args.copy_probe_mb)
     L, pb, inp = res["L"], res["pb"], res["inp"]
+    q_dev, k_dev, v_dev, a_dev = res.pop("dev_tensors")
     stage_ms, kern_ms, pairs = res["stage_ms"], res["kern_ms"], res["pairs"]
     dev = torch.device("cuda:0")
     d = cfg.d
@@ -643,6 +644,43 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    # the HBM-bound stages again with the 256 MB Infinity Cache evicted before every repetition,
+    # each timed alone: kernel (library events) and stage (call).  The eviction reads 1 GiB (a
+    # write would leave the cache full of dirty lines, whose write-back the timed kernel pays for)
+    if not args.block_io:
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        calls = {
+            "zone_stats": ("k_zone_stats", lambda: P.prism_zone_stats(pb, v_dev, a_dev, cfg.eps, L.g, L.rho,
+                                                                      L.zone_audio)),
+            "permute_pool": ("k_permute_pool", lambda: P.prism_permute_pool(
+                pb, L.shape_idx, L.zone_block_off, [q_dev, k_dev, v_dev], [L.qp, L.kp, L.vp],
+                [L.qbar, L.kbar, None])),
+        }
+        cold = {}
+        for st_name, (kn, fn) in calls.items():
+            ks, ss = [], []
+            for r in range(7):
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                for e in evs:
+                    e.record()
+                flush.sum()
+                P.prism_trace_kernel(kn, evs[2], evs[3])
+                evs[0].record()
+                fn()
+                evs[1].record()
+                torch.cuda.synchronize()
+                P.prism_trace_kernel(None)
+                ss.append(evs[0].elapsed_time(evs[1]))
+                ks.append(evs[2].elapsed_time(evs[3]))
+            km_, sm_ = sorted(ks)[len(ks) // 2], sorted(ss)[len(ss) // 2]
+            nbytes = kbytes[kn]
+            cold[st_name] = {"kernel_ms": round(km_, 4), "stage_ms": round(sm_, 4),
+                             "kernel_frac": round(nbytes / (km_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "stage_frac": round(nbytes / (sm_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del flush
+        out["hbm_stages_cold"] = {"note": "median of 7 repetitions, a 1 GiB read before each (evicts the "
+                                          "256 MB Infinity Cache)", **cold}
     # auxiliary, not part of the step: the audio-norm producer (the next layer's coupling input)
     # on a cross-attention output of this GPU's heads x d channels, device-generated
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -663,7 +701,7 @@ def main():
     out["aux_stages"] = {"audio_norms": {"ms": round(an_ms, 4), "channels": H_ * d,
                                          "GB/s": round(an_bytes / (an_ms * 1e-3) / 1e9, 1),
                                          "frac": round(an_bytes / (an_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
-    del hh, an, L
+    del hh, an, L, q_dev, k_dev, v_dev, a_dev
     res.pop("L")
     torch.cuda.empty_cache()
     # the other workloads, each timed the same way with fewer steps (one line, one run)
@@ -677,6 +715,7 @@ def main():
             c2 = cfg if reuse else synth.CONFIGS[name]
             r2 = measure(c2, steps, warm, detail=False, inp=inp if reuse else None, **kw)
             r2.pop("L")
+            r2.pop("dev_tensors")
             sm2 = summary(r2)
             sm2["steps"] = steps
             if name == "tiny":
