@@ -30,6 +30,9 @@ SMALL = {
     # expands most lists far beyond k (the pages' dispersed-attention case)
     "stress_small": synth.Config("stress_small", 16, 16, 32, 2, 128, "bf16", blobs=2, k_abs=0, k_frac=0.02,
                                  p=0.95, backward=True, seed=2004, amp_v=0.1, gamma=16.0 * 0.3),
+    # the smallest grid: one 8x8x8 zone (2 to 8 blocks, 8 atoms and 4 atom pairs per head)
+    "one_zone": synth.Config("one_zone", 8, 8, 8, 2, 128, "bf16", blobs=1, k_abs=1, k_frac=0.0, p=0.5,
+                             backward=True, seed=2005),
 }
 
 
