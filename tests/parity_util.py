@@ -22,8 +22,13 @@ NEAR_TIE_CAP = 1e-3   # near-tie mismatches allowed, as a fraction of cases (rou
 
 
 def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
+    """Progress and result lines of the parity checks, shown as they happen (also under -q)."""
+    line = " ".join(str(x) for x in a)
+    conftest = sys.modules.get("conftest")
+    if conftest is not None and hasattr(conftest, "progress"):
+        conftest.progress(line)
+    else:
+        print(line, flush=True)
 
 
 def problem_of(cfg: synth.Config):
