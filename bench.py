@@ -252,9 +252,10 @@ def cpu_baseline(inp, budget_s=20.0):
             **host_record()}
 
 
-def write_traffic(d, probe_mb, config):
+def write_traffic(d, probe_mb, config, out_path=None):
     """HBM bytes per dispatch from two rocprofv3 --pmc runs.  The counters are scaled by what
-    they read for the known-size device copy (probe_mb MiB read and written) in the same run."""
+    they read for the known-size device copy (probe_mb MiB read and written) in the same run.
+    Written to out_path (default profiles/traffic.json)."""
     import csv
     import glob
 
@@ -296,7 +297,7 @@ def write_traffic(d, probe_mb, config):
     meta = {"fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "probe_bytes": probe,
             "note": "bytes = counter KiB x 1024 x scale; scale = probe bytes / counter bytes of the probe copy"}
     out = {"_calibration": meta, **res}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(out_path or os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({k: v.get("bytes_per_launch") for k, v in res.items()}))
 
