@@ -27,7 +27,9 @@ def progress(line):
         return
     with capman.global_and_fixture_disabled():
         tr.write_line(line)
-        tr._tw.flush()
+        tw = getattr(tr, "_tw", None)  # the reporter's terminal writer, flushed when present
+        if tw is not None:
+            tw.flush()
 
 
 def pytest_terminal_summary(terminalreporter):
