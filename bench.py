@@ -648,40 +648,43 @@ def main():
     # the HBM-bound stages again with the 256 MB Infinity Cache evicted before every repetition,
     # each timed alone: kernel (library events) and stage (call).  The eviction reads 1 GiB (a
     # write would leave the cache full of dirty lines, whose write-back the timed kernel pays for)
-    if not args.block_io:
-        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-        torch.cuda.synchronize()
-        calls = {
-            "zone_stats": ("k_zone_stats", lambda: P.prism_zone_stats(pb, v_dev, a_dev, cfg.eps, L.g, L.rho,
-                                                                      L.zone_audio)),
-            "permute_pool": ("k_permute_pool", lambda: P.prism_permute_pool(
-                pb, L.shape_idx, L.zone_block_off, [q_dev, k_dev, v_dev], [L.qp, L.kp, L.vp],
-                [L.qbar, L.kbar, None])),
-        }
-        cold = {}
-        for st_name, (kn, fn) in calls.items():
-            ks, ss = [], []
-            for r in range(7):
-                evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                for e in evs:
-                    e.record()
-                flush.sum()
-                P.prism_trace_kernel(kn, evs[2], evs[3])
-                evs[0].record()
-                fn()
-                evs[1].record()
-                torch.cuda.synchronize()
-                P.prism_trace_kernel(None)
-                ss.append(evs[0].elapsed_time(evs[1]))
-                ks.append(evs[2].elapsed_time(evs[3]))
-            km_, sm_ = sorted(ks)[len(ks) // 2], sorted(ss)[len(ss) // 2]
-            nbytes = kbytes[kn]
-            cold[st_name] = {"kernel_ms": round(km_, 4), "stage_ms": round(sm_, 4),
-                             "kernel_frac": round(nbytes / (km_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "stage_frac": round(nbytes / (sm_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        del flush
-        out["hbm_stages_cold"] = {"note": "median of 7 repetitions, a 1 GiB read before each (evicts the "
-                                          "256 MB Infinity Cache)", **cold}
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    calls = {"zone_stats": ("k_zone_stats", lambda: P.prism_zone_stats(pb, v_dev, a_dev, cfg.eps, L.g, L.rho,
+                                                                       L.zone_audio))}
+    if args.block_io:
+        calls["permute_qkv"] = ("k_permute", lambda: P.prism_permute(pb, L.shape_idx, 0, [q_dev, k_dev, v_dev],
+                                                                     [L.qp, L.kp, L.vp]))
+        calls["pool"] = ("k_pool", lambda: P.prism_pool_blocks(pb, L.block_start, [L.qp, L.kp],
+                                                               [L.qbar, L.kbar]))
+    else:
+        calls["permute_pool"] = ("k_permute_pool", lambda: P.prism_permute_pool(
+            pb, L.shape_idx, L.zone_block_off, [q_dev, k_dev, v_dev], [L.qp, L.kp, L.vp],
+            [L.qbar, L.kbar, None]))
+    cold = {}
+    for st_name, (kn, fn) in calls.items():
+        ks, ss = [], []
+        for r in range(7):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for e in evs:
+                e.record()
+            flush.sum()
+            P.prism_trace_kernel(kn, evs[2], evs[3])
+            evs[0].record()
+            fn()
+            evs[1].record()
+            torch.cuda.synchronize()
+            P.prism_trace_kernel(None)
+            ss.append(evs[0].elapsed_time(evs[1]))
+            ks.append(evs[2].elapsed_time(evs[3]))
+        km_, sm_ = sorted(ks)[len(ks) // 2], sorted(ss)[len(ss) // 2]
+        nbytes = kbytes[kn]
+        cold[st_name] = {"kernel_ms": round(km_, 4), "stage_ms": round(sm_, 4),
+                         "kernel_frac": round(nbytes / (km_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "stage_frac": round(nbytes / (sm_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del flush
+    out["hbm_stages_cold"] = {"note": "median of 7 repetitions, a 1 GiB read before each (evicts the "
+                                      "256 MB Infinity Cache)", **cold}
     # auxiliary, not part of the step: the audio-norm producer (the next layer's coupling input)
     # on a cross-attention output of this GPU's heads x d channels, device-generated
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
