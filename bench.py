@@ -306,7 +306,7 @@ def write_traffic(d, probe_mb, config, out_path=None):
 # forward's S and its split PV (3 products of 2d FLOP), the dQ kernel's recomputed S and dP
 # plus its split dQ (4), the dK/dV kernel's S, dP, split dV and split dK (6).
 ISSUED_PER_PAIR = {"k_fwd": 6.0, "k_dq": 8.0, "k_dkdv": 12.0}
-# Algorithmic FLOPs per pair (SURVEY convention: F_fwd = 4d per pair, F_bwd = 2.5 F_fwd with the
+# Algorithmic FLOPs per pair (the convention F_fwd = 4d per pair, F_bwd = 2.5 F_fwd with the
 # recomputed S among the five backward products): the forward's QK^T and PV; the dK/dV kernel's
 # S, dP, dV and dK; the dQ kernel's dQ product (its S and dP repeat the dK/dV kernel's).
 ALG_PER_PAIR = {"k_fwd": 4.0, "k_dq": 2.0, "k_dkdv": 8.0}
