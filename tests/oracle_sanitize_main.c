@@ -67,7 +67,7 @@ int main(void) {
   int32_t* nblocks = malloc(sizeof(int32_t) * groups);
   CHECK(orc_block_layout(T, H, W, groups, shape_idx, pos, bs, nblocks));
 
-  /* block-order copies: the oracle's permutation is pos; the driver only moves rows */
+  /* block-order copies: the oracle's permutation is pos; this program only moves rows */
   float* qp = malloc(sizeof(float) * heads * N * d);
   float* kp = malloc(sizeof(float) * heads * N * d);
   float* vp = malloc(sizeof(float) * heads * N * d);
