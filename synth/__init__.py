@@ -95,6 +95,10 @@ CONFIGS = {
     # million tokens"), otherwise the 2K headline's settings
     "1m": Config("1m", 64, 128, 128, 4, 128, "bf16", blobs=6, k_abs=0, k_frac=0.05, p=0.9,
                  backward=True, seed=1006),
+    # the head-dim-64 kernels at a full grid: 720p-shaped, 8 heads, forward + backward; gamma
+    # scaled by sqrt(64/128) so that sm_scale matches the head-dim-128 configs
+    "720p_d64": Config("720p_d64", 24, 48, 80, 8, 64, "bf16", blobs=3, k_abs=0, k_frac=0.05, p=0.9,
+                       backward=True, seed=1007, gamma=16.0 / math.sqrt(2.0)),
 }
 
 

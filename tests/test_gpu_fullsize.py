@@ -1,6 +1,6 @@
-"""GPU parity at the full configured sizes (720p-, 1080p-, 2K-shaped grids, the 2K stress case
-and the largest grid, 64x128x128 = 1,048,576 tokens in 2048 zones), in the launch configuration
-the benchmark times.
+"""GPU parity at the full configured sizes (720p-, 1080p-, 2K-shaped grids, the 2K stress case,
+the largest grid, 64x128x128 = 1,048,576 tokens in 2048 zones, and the 720p grid with head dim
+64 and a backward), in the launch configuration the benchmark times.
 
 Zone statistics, shapes and the complete selection are compared against the oracle over
 every zone and every query block.  Attention outputs and gradients, given the oracle's
@@ -9,7 +9,7 @@ dQ on random query blocks of every head (the C oracle), dK and dV on chosen key 
 every head (the fp64 matrix-product oracle, oracle/attn_rows.py, whose cost grows with the
 number of query blocks that selected the key block):
 
-* 1080p, 2K and the 1,048,576-token grid: one rarely selected key block (at most 24 selecting
+* 1080p, 720p at head dim 64, 2K and the 1,048,576-token grid: one rarely selected key block (at most 24 selecting
   query blocks), the key block at the median selector count (the largest grid: first head
   only), and one of the heavy key blocks that the backward's launch order moves to the front
   (selected by more than 2.5 times the mean; the least selected of them, 2K every head, 1080p
@@ -28,7 +28,7 @@ from parity_util import (LSE_ABS, Run, assert_close_attn, cap, compare_masks, co
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["720p", "1080p", "2k", "2k_stress", "1m"]
+FULL = ["720p", "1080p", "2k", "2k_stress", "1m", "720p_d64"]
 QB_PER_HEAD = 3
 HEAVY = 2.5  # the backward launch order's threshold for dK/dV work (times the mean per atom)
 
