@@ -3,9 +3,9 @@ the smoke check).  This module holds no arithmetic of the method itself: it only
 token fields, audio norms and output gradients, and rounds them to the compute dtype.
 
 Workloads.  The pages train and evaluate on private 720p/1080p/2K video latents and on a
-300-video 2K benchmark; none is available, so these token grids stand in for them (a 2K
-clip gives "hundreds of thousands to over one million tokens" per the reading guide's
-"Problem and motivation").  Per config i (1..6) the generator uses
+300-video 2K benchmark; none is available, so these token grids stand in for them (at 2K a
+clip is a few hundred thousand to more than a million tokens long, reading guide, "Problem
+and motivation").  Per config i (1..7) the generator uses
 ``np.random.SeedSequence(1000 + i).spawn(8)``, one child per array in the order
 f, phi, noise_Q, noise_K, noise_V, audio centres, audio noise, dO (PCG64 each).
 
@@ -91,8 +91,8 @@ CONFIGS = {
     # scaled by 0.3, k = 2 %, p = 0.95
     "2k_stress": Config("2k_stress", 32, 96, 160, 4, 128, "bf16", blobs=6, k_abs=0, k_frac=0.02,
                         p=0.95, backward=True, seed=1005, amp_v=0.1, gamma=16.0 * 0.3),
-    # the largest grid the library takes: 2048 zones, 1,048,576 tokens (a 2K clip "over one
-    # million tokens"), otherwise the 2K headline's settings
+    # the largest grid the library takes: 2048 zones, 1,048,576 tokens (the long end of a 2K
+    # clip), otherwise the 2K headline's settings
     "1m": Config("1m", 64, 128, 128, 4, 128, "bf16", blobs=6, k_abs=0, k_frac=0.05, p=0.9,
                  backward=True, seed=1006),
     # the head-dim-64 kernels at a full grid: 720p-shaped, 8 heads, forward + backward; gamma
