@@ -1,5 +1,6 @@
 """Host logic of bench.py (no GPU): the one-GPU guard, the counter-to-bytes conversion behind
-roofline.traffic, the FLOP conventions and the per-configuration roofline arithmetic."""
+roofline.traffic, the FLOP conventions, the per-configuration roofline arithmetic and the
+executed query-key pair count every FLOP figure is built on."""
 import csv
 import json
 import os
@@ -86,3 +87,46 @@ def test_summary_roofline_arithmetic():
     assert s["roofline"]["achieved"] == round(want, 1)
     assert s["roofline"]["frac"] == round(want / bench.PEAK_BF16_TFLOPS, 4)
     assert s["attn_mfma_frac"] == round(res["attn_tflops"] / bench.PEAK_BF16_TFLOPS, 4)
+
+
+def test_executed_pairs_by_brute_force():
+    """selection_stats against a direct count over token pairs on a hand-built two-zone layout:
+    every (query token, key token) pair whose key block is in the query block's list."""
+    import types
+
+    import numpy as np
+    import torch
+
+    N = 1024
+    sizes = [64] * 8 + [256, 256]          # zone 0: eight 64-row blocks; zone 1: two 256-row blocks
+    nb, nbmax = len(sizes), 8 * (N // 512)
+    bs = torch.full((1, nbmax + 1), N, dtype=torch.int32)
+    bs[0, 0] = 0
+    bs[0, 1:nb + 1] = torch.tensor(sizes, dtype=torch.int32).cumsum(0)
+    rng = np.random.default_rng(3)
+    heads = 2
+    cnt = torch.zeros(heads, nbmax, dtype=torch.int32)
+    idx = torch.zeros(heads, nbmax, nbmax, dtype=torch.int32)
+    lists = {}
+    for h in range(heads):
+        for i in range(nb):
+            l = sorted(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+            lists[h, i] = l
+            cnt[h, i] = len(l)
+            idx[h, i, :len(l)] = torch.tensor(l, dtype=torch.int32)
+            idx[h, i, len(l):] = 5                # stale entries past the count must be ignored
+    shape_idx = torch.tensor([[3, 13]], dtype=torch.uint8)  # a 64-row shape and a 256-row shape
+    layer = types.SimpleNamespace(block_start=bs, sel_count=cnt, sel_idx=idx, shape_idx=shape_idx)
+    pb = types.SimpleNamespace(N=N, heads=heads, groups=1, nbmax=nbmax)
+    pairs, key_frac, hist, nblocks = bench.selection_stats(layer, pb)
+
+    block_of = np.repeat(np.arange(nb), sizes)
+    want, fr = 0, []
+    for h in range(heads):
+        keyset = [set(lists[h, i]) for i in range(nb)]
+        allowed = np.array([[block_of[c] in keyset[block_of[r]] for c in range(N)] for r in range(0, N, 64)])
+        want += int(allowed.sum()) * 64    # rows come in 64-row groups of one block each
+        fr.append(np.mean([sum(sizes[j] for j in lists[h, i]) / N for i in range(nb)]))
+    assert pairs == want
+    assert abs(key_frac - float(np.mean(fr))) < 1e-12
+    assert hist == {64: 1, 128: 0, 256: 1} and nblocks == nb
